@@ -1,0 +1,304 @@
+// C ABI of libgqa.so: argument checks, split planning and kernel dispatch.
+//
+// Everything here runs on the host.  Invalid calls are rejected before any
+// HIP runtime call, so the checks can be exercised on a machine without a GPU.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/gqa.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gqa_status fail(gqa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+gqa_status ok() { return GQA_OK; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Split planning.  The decode kernels run one workgroup per (sequence,
+// K/V head, split).  Enough workgroups are wanted to keep all 256 compute
+// units streaming (a few resident per CU), but each split should be long
+// enough that its partial result (d + 2 floats per head, written and read
+// back once) stays small next to the K/V bytes it covers.  Long caches are cut
+// into bounded slices so that ragged lengths balance across the machine.
+constexpr int64_t kTargetWorkgroups = 1024;
+constexpr int64_t kMinSplitLen = 128;
+constexpr int64_t kMaxSplitLen = 2048;
+
+bool decode_shape_valid(int B, int H, int G, int d, int n_max) {
+  if (B < 0 || n_max < 0 || d < 1) return false;
+  if (B == 0) return true;
+  if (H < 1 || G < 1 || H % G != 0) return false;
+  return true;
+}
+
+int plan_splits(int B, int G, int n_max) {
+  if (B <= 0 || n_max <= 0) return 1;
+  const int64_t units = int64_t(B) * G;
+  int64_t s = ceil_div(kTargetWorkgroups, units);
+  s = std::max<int64_t>(s, ceil_div(n_max, kMaxSplitLen));
+  s = std::min<int64_t>(s, std::max<int64_t>(1, ceil_div(n_max, kMinSplitLen)));
+  // round the slice length to whole 32-position tiles
+  int64_t len = ceil_div(ceil_div(n_max, s), 32) * 32;
+  return int(ceil_div(n_max, len));
+}
+
+// Splits are whole 32-position tiles except possibly the last; the count
+// actually used for a requested count S.
+void split_geometry(int n_max, int S, int* S_used, int* split_len) {
+  if (n_max <= 0 || S <= 1) {
+    *S_used = 1;
+    *split_len = std::max(n_max, 1);
+    return;
+  }
+  int64_t len = ceil_div(n_max, S);
+  if (len >= 32) len = ceil_div(len, 32) * 32;
+  *split_len = int(len);
+  *S_used = int(ceil_div(n_max, len));
+}
+
+size_t workspace_for(int B, int H, int d, int S) {
+  if (S <= 1 || B <= 0) return 0;
+  const size_t rows = size_t(B) * size_t(H) * size_t(S);
+  const size_t o_bytes = rows * size_t(d) * sizeof(float);
+  const size_t ml_bytes = rows * 2 * sizeof(float);
+  return ((o_bytes + 255) / 256) * 256 + ml_bytes;
+}
+
+gqa_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(GQA_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_t* seqlens,
+                       void* out, int B, int H, int G, int d, int n_max, float scale, int dtype,
+                       int num_splits, void* ws, size_t ws_bytes, void* stream_v) {
+  g_last_error.clear();
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_INVALID_ARG, "gqa_decode: unknown dtype %d", dtype);
+  if (B < 0 || n_max < 0)
+    return fail(GQA_ERR_INVALID_ARG, "gqa_decode: negative size (B=%d, n_max=%d)", B, n_max);
+  if (B == 0) return ok();
+  if (H < 1 || G < 1)
+    return fail(GQA_ERR_INVALID_ARG, "gqa_decode: H=%d and G=%d must be >= 1", H, G);
+  if (H % G != 0)
+    return fail(GQA_ERR_INVALID_ARG, "gqa_decode: H=%d is not a multiple of G=%d", H, G);
+  if (d < 1) return fail(GQA_ERR_INVALID_ARG, "gqa_decode: head size d=%d", d);
+  if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "gqa_decode: scale is not finite");
+  if (num_splits < 0) return fail(GQA_ERR_INVALID_ARG, "gqa_decode: num_splits=%d", num_splits);
+  if (!q || !out || !seqlens || (n_max > 0 && (!k || !v)))
+    return fail(GQA_ERR_INVALID_ARG, "gqa_decode: NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(out) || (n_max > 0 && (!aligned16(k) || !aligned16(v))) ||
+      (reinterpret_cast<uintptr_t>(seqlens) & 3u))
+    return fail(GQA_ERR_INVALID_ARG, "gqa_decode: tensors must be 16-byte aligned");
+  if (d != 64 && d != 128)
+    return fail(GQA_ERR_UNSUPPORTED, "gqa_decode: head size d=%d (built for 64 and 128)", d);
+  const int64_t n_rows64 = int64_t(B) * H;
+  if (n_rows64 * d > (int64_t(1) << 40) || int64_t(B) * G * n_max > (int64_t(1) << 40))
+    return fail(GQA_ERR_INVALID_ARG, "gqa_decode: problem too large");
+
+  int S_req = num_splits == 0 ? plan_splits(B, G, n_max) : std::min(num_splits, std::max(n_max, 1));
+  int S, split_len;
+  split_geometry(n_max, S_req, &S, &split_len);
+  const size_t need = workspace_for(B, H, d, S);
+  if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned16(ws)))
+    return fail(GQA_ERR_WORKSPACE, "gqa_decode: workspace of %zu bytes needed, %zu given%s", need,
+                ws_bytes, (ws && !aligned16(ws)) ? " (misaligned)" : "");
+
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (need > 0) {
+    part_o = static_cast<float*>(ws);
+    const size_t o_bytes = size_t(B) * H * S * d * sizeof(float);
+    part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ((o_bytes + 255) / 256) * 256);
+  }
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  const int n_rep = H / G;
+
+  if (dtype == GQA_DTYPE_BF16 && gqa::decode_mfma_supports(n_rep, d)) {
+    gqa::DecodeProblem p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.seqlens = seqlens;
+    p.out = static_cast<uint16_t*>(out);
+    p.part_o = part_o;
+    p.part_ml = part_ml;
+    p.B = B; p.H = H; p.G = G; p.n_rep = n_rep; p.d = d; p.n_max = n_max;
+    p.scale = scale;
+    p.num_splits = S;
+    p.split_len = split_len;
+    gqa_status st = launched(gqa::launch_decode_mfma(p, stream), "gqa_decode");
+    if (st != GQA_OK) return st;
+  } else {
+    gqa::RowsProblem p{};
+    p.q = q; p.k = k; p.v = v; p.seqlens = seqlens; p.out = out;
+    p.part_o = part_o; p.part_ml = part_ml;
+    p.n_rows = B; p.rows_per_batch = 1;
+    p.H = H; p.G = G; p.n_rep = n_rep; p.d = d;
+    p.q_row_stride = int64_t(H) * d;
+    p.kv_batch_stride = int64_t(G) * n_max * d;
+    p.kv_group_stride = int64_t(n_max) * d;
+    p.kv_pos_stride = d;
+    p.n_max = n_max;
+    p.causal = 0;
+    p.scale = scale;
+    p.num_splits = S;
+    p.split_len = split_len;
+    gqa_status st = launched(gqa::launch_rows_valu(p, dtype, stream), "gqa_decode");
+    if (st != GQA_OK) return st;
+  }
+  if (S > 1) {
+    gqa::CombineProblem c{};
+    c.part_o = part_o; c.part_ml = part_ml; c.out = out;
+    c.n_rows = B; c.H = H; c.d = d; c.num_splits = S; c.dtype = dtype;
+    return launched(gqa::launch_combine(c, stream), "gqa_decode (combine)");
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_decode_num_splits(int B, int H, int G, int d, int n_max) {
+  if (!decode_shape_valid(B, H, G, d, n_max)) return 0;
+  int S, len;
+  split_geometry(n_max, plan_splits(B, G, n_max), &S, &len);
+  return S;
+}
+
+size_t gqa_decode_workspace_bytes(int B, int H, int G, int d, int n_max, int num_splits) {
+  if (!decode_shape_valid(B, H, G, d, n_max) || num_splits < 0) return size_t(-1);
+  int S_req = num_splits == 0 ? plan_splits(B, G, n_max) : std::min(num_splits, std::max(n_max, 1));
+  int S, len;
+  split_geometry(n_max, S_req, &S, &len);
+  return workspace_for(B, H, d, S);
+}
+
+gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seqlens, void* out, int B, int H, int G, int d, int n_max,
+                      float scale, int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return decode_impl(q, k_cache, v_cache, seqlens, out, B, H, G, d, n_max, scale, dtype, 0,
+                     workspace, workspace_bytes, stream);
+}
+
+gqa_status gqa_decode_split(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seqlens, void* out, int B, int H, int G, int d,
+                            int n_max, float scale, int dtype, int num_splits, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, seqlens, out, B, H, G, d, n_max, scale, dtype,
+                     num_splits, workspace, workspace_bytes, stream);
+}
+
+gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void* out, int B,
+                              int T, int H, int G, int d, float scale, int dtype, void* stream_v) {
+  g_last_error.clear();
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: unknown dtype %d", dtype);
+  if (B < 0 || T < 0)
+    return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: negative size (B=%d, T=%d)", B, T);
+  if (B == 0 || T == 0) return ok();
+  if (H < 1 || G < 1)
+    return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: H=%d and G=%d must be >= 1", H, G);
+  if (H % G != 0)
+    return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: H=%d is not a multiple of G=%d", H, G);
+  if (d < 1) return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: head size d=%d", d);
+  if (!std::isfinite(scale))
+    return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: scale is not finite");
+  if (!q || !k || !v || !out) return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: NULL tensor");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: tensors must be 16-byte aligned");
+  if (d != 64 && d != 128)
+    return fail(GQA_ERR_UNSUPPORTED, "gqa_prefill_causal: head size d=%d (built for 64 and 128)", d);
+  if (int64_t(B) * T * H * d > (int64_t(1) << 40))
+    return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: problem too large");
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  const int n_rep = H / G;
+  if (dtype == GQA_DTYPE_BF16 && gqa::prefill_mfma_supports(n_rep, d)) {
+    gqa::PrefillProblem p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.out = static_cast<uint16_t*>(out);
+    p.B = B; p.T = T; p.H = H; p.G = G; p.n_rep = n_rep; p.d = d;
+    p.scale = scale;
+    return launched(gqa::launch_prefill_mfma(p, stream), "gqa_prefill_causal");
+  }
+  gqa::RowsProblem p{};
+  p.q = q; p.k = k; p.v = v; p.seqlens = nullptr; p.out = out;
+  p.n_rows = B * T; p.rows_per_batch = T;
+  p.H = H; p.G = G; p.n_rep = n_rep; p.d = d;
+  p.q_row_stride = int64_t(H) * d;
+  p.kv_batch_stride = int64_t(T) * G * d;
+  p.kv_group_stride = d;
+  p.kv_pos_stride = int64_t(G) * d;
+  p.n_max = T;
+  p.causal = 1;
+  p.scale = scale;
+  p.num_splits = 1;
+  p.split_len = T;
+  return launched(gqa::launch_rows_valu(p, dtype, stream), "gqa_prefill_causal");
+}
+
+gqa_status kv_meanpool_heads(const void* w_in, void* w_out, int H, int G, int64_t per_head_elems,
+                             int dtype, void* stream_v) {
+  g_last_error.clear();
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: unknown dtype %d", dtype);
+  if (H < 1 || G < 1 || H % G != 0)
+    return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: H=%d must be a positive multiple of G=%d",
+                H, G);
+  if (per_head_elems < 0)
+    return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: per_head_elems=%lld",
+                (long long)per_head_elems);
+  if (per_head_elems == 0) return ok();
+  if (!w_in || !w_out) return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: NULL tensor");
+  if (!aligned16(w_in) || !aligned16(w_out))
+    return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: tensors must be 16-byte aligned");
+  if (int64_t(H) * per_head_elems > (int64_t(1) << 40))
+    return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: problem too large");
+  gqa::MeanpoolProblem p{};
+  p.w_in = w_in; p.w_out = w_out; p.H = H; p.G = G; p.n_rep = H / G;
+  p.per_head_elems = per_head_elems; p.dtype = dtype;
+  return launched(gqa::launch_meanpool(p, static_cast<hipStream_t>(stream_v)),
+                  "kv_meanpool_heads");
+}
+
+const char* gqa_status_string(int status) {
+  switch (status) {
+    case GQA_OK: return "GQA_OK";
+    case GQA_ERR_INVALID_ARG: return "GQA_ERR_INVALID_ARG";
+    case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED";
+    case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE";
+    case GQA_ERR_LAUNCH: return "GQA_ERR_LAUNCH";
+    default: return "GQA_ERR_UNKNOWN";
+  }
+}
+
+const char* gqa_last_error(void) { return g_last_error.c_str(); }
+
+int gqa_version(void) { return 100; }
+
+}  // extern "C"

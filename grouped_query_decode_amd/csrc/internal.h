@@ -1,0 +1,84 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+
+// Generic "rows of queries attend a K/V head" problem, used by the vector-unit
+// kernel for decode (one row per sequence) and for float32 causal prefill (one
+// row per prompt position).  All strides are in elements.
+struct RowsProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seqlens;   // decode only (causal == 0)
+  void* out;
+  float* part_o;            // [rows, H, S, d] float32, when S > 1
+  float* part_ml;           // [rows, H, S, 2] (running max, normaliser), when S > 1
+  int n_rows;               // decode: B; prefill: B*T
+  int rows_per_batch;       // decode: 1; prefill: T
+  int H, G, n_rep, d;
+  int64_t q_row_stride;     // between consecutive rows (q and out)
+  int64_t kv_batch_stride;  // between batches
+  int64_t kv_group_stride;  // between K/V heads
+  int64_t kv_pos_stride;    // between cached positions
+  int n_max;                // decode: cache capacity; prefill: T
+  int causal;               // 0: length from seqlens; 1: row i attends 0..i
+  float scale;
+  int num_splits;           // S
+  int split_len;            // positions per split
+};
+
+// Batched decode on the matrix cores (bf16 only).
+struct DecodeProblem {
+  const uint16_t* q;        // [B, H, d]
+  const uint16_t* k;        // [B, G, n_max, d]
+  const uint16_t* v;
+  const int32_t* seqlens;
+  uint16_t* out;            // [B, H, d]
+  float* part_o;
+  float* part_ml;
+  int B, H, G, n_rep, d, n_max;
+  float scale;
+  int num_splits, split_len;
+};
+
+struct CombineProblem {
+  const float* part_o;
+  const float* part_ml;
+  void* out;                // [rows, H, d] in dtype
+  int n_rows, H, d, num_splits;
+  int dtype;
+};
+
+struct PrefillProblem {
+  const uint16_t* q;        // [B, T, H, d]
+  const uint16_t* k;        // [B, T, G, d]
+  const uint16_t* v;
+  uint16_t* out;            // [B, T, H, d]
+  int B, T, H, G, n_rep, d;
+  float scale;
+};
+
+struct MeanpoolProblem {
+  const void* w_in;
+  void* w_out;
+  int H, G, n_rep;
+  int64_t per_head_elems;
+  int dtype;
+};
+
+// Launchers: each returns hipSuccess or the launch error.
+hipError_t launch_rows_valu(const RowsProblem& p, int dtype, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeProblem& p, hipStream_t stream);
+bool decode_mfma_supports(int n_rep, int d);
+hipError_t launch_combine(const CombineProblem& p, hipStream_t stream);
+hipError_t launch_prefill_mfma(const PrefillProblem& p, hipStream_t stream);
+bool prefill_mfma_supports(int n_rep, int d);
+hipError_t launch_meanpool(const MeanpoolProblem& p, hipStream_t stream);
+
+}  // namespace gqa

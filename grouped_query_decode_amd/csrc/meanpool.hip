@@ -1,0 +1,114 @@
+// kv_meanpool_heads: MHA -> GQA conversion of one K or V projection.
+//
+// GQA paper section 2.1 (Figure 1) and section 2.2; 2kiu.com tutorial section
+// 4.3, step 2: each group's key (or value) projection is the mean of its member
+// heads' projections.  Groups are consecutive blocks of n_rep heads.
+//
+// HBM-bound: every input element is read once and every output element
+// written once.  Each thread owns 8 consecutive elements of one group's output
+// (16-byte bfloat16 or 2 x 16-byte float32 accesses), reads the same 8 elements
+// of the group's n_rep heads, sums in float32, divides once (correctly
+// rounded) and rounds once to the storage type.  A grid-stride loop covers the
+// output; a scalar kernel handles sizes that are not a multiple of 8.
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace gqa {
+namespace {
+
+template <int DT>
+__global__ __launch_bounds__(256) void meanpool_vec8_kernel(MeanpoolProblem p) {
+  const int64_t vec_per_head = p.per_head_elems / 8;
+  const int64_t total = int64_t(p.G) * vec_per_head;
+  const float inv_div = float(p.n_rep);
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t g = i / vec_per_head;
+    const int64_t e8 = i - g * vec_per_head;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < p.n_rep; ++k) {
+      const int64_t elem = (g * p.n_rep + k) * p.per_head_elems + e8 * 8;
+      if (DT == kBF16) {
+        const u32x4_t w = ld16(static_cast<const uint16_t*>(p.w_in) + elem);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          acc[2 * t] += bf16lo_to_f32(w[t]);
+          acc[2 * t + 1] += bf16hi_to_f32(w[t]);
+        }
+      } else {
+        const float* src = static_cast<const float*>(p.w_in) + elem;
+        const u32x4_t a = ld16(src);
+        const u32x4_t b = ld16(src + 4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          acc[t] += __uint_as_float(a[t]);
+          acc[4 + t] += __uint_as_float(b[t]);
+        }
+      }
+    }
+    const int64_t oel = g * p.per_head_elems + e8 * 8;
+    if (DT == kBF16) {
+      u32x4_t w;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(acc[2 * t] / inv_div, acc[2 * t + 1] / inv_div);
+      st16(static_cast<uint16_t*>(p.w_out) + oel, w);
+    } else {
+      u32x4_t a, b;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        a[t] = __float_as_uint(acc[t] / inv_div);
+        b[t] = __float_as_uint(acc[4 + t] / inv_div);
+      }
+      float* dst = static_cast<float*>(p.w_out) + oel;
+      st16(dst, a);
+      st16(dst + 4, b);
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void meanpool_scalar_kernel(MeanpoolProblem p) {
+  const int64_t total = int64_t(p.G) * p.per_head_elems;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t g = i / p.per_head_elems;
+    const int64_t e = i - g * p.per_head_elems;
+    float acc = 0.f;
+    for (int k = 0; k < p.n_rep; ++k) {
+      const int64_t elem = (g * p.n_rep + k) * p.per_head_elems + e;
+      acc += DT == kBF16 ? bf16_to_f32(static_cast<const uint16_t*>(p.w_in)[elem])
+                         : static_cast<const float*>(p.w_in)[elem];
+    }
+    const float mean = acc / float(p.n_rep);
+    if (DT == kBF16)
+      static_cast<uint16_t*>(p.w_out)[i] = to_bf16(mean);
+    else
+      static_cast<float*>(p.w_out)[i] = mean;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_meanpool(const MeanpoolProblem& p, hipStream_t stream) {
+  const bool vec = (p.per_head_elems % 8) == 0;
+  const int64_t work = vec ? int64_t(p.G) * (p.per_head_elems / 8) : int64_t(p.G) * p.per_head_elems;
+  // enough threads to cover the output once, capped (grid-stride beyond)
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  if (blocks < 1) blocks = 1;
+  if (vec) {
+    if (p.dtype == kBF16)
+      hipLaunchKernelGGL(meanpool_vec8_kernel<kBF16>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL(meanpool_vec8_kernel<kF32>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  } else {
+    if (p.dtype == kBF16)
+      hipLaunchKernelGGL(meanpool_scalar_kernel<kBF16>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL(meanpool_scalar_kernel<kF32>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gqa

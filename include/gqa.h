@@ -1,0 +1,184 @@
+/*
+ * gqa.h - C ABI of libgqa.so: grouped-query attention on AMD MI355X (gfx950).
+ *
+ * Grouped-query attention (GQA paper, "GQA: Training Generalized Multi-Query
+ * Transformer Models from Multi-Head Checkpoints", section 2.2): H query heads
+ * are split into G groups and every group shares one key head and one value
+ * head.  G = H is multi-head attention, G = 1 is multi-query attention.  Query
+ * head h uses K/V head floor(h * G / H): the groups are consecutive blocks of
+ * n_rep = H / G heads, as in the 2kiu.com MHA/MQA/GQA tutorial's example of 8
+ * heads in 2 groups (section 3.1: heads 1-4 share group 1, heads 5-8 group 2).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Tensor arguments are DEVICE pointers owned by the caller, dense and
+ *   row-major in the shapes given below, each 16-byte aligned.  The library
+ *   never allocates, frees or keeps them after the call returns.
+ * - dtype is GQA_DTYPE_F32 (float) or GQA_DTYPE_BF16 (bfloat16); inputs and
+ *   outputs share it.  Arithmetic is float32 throughout; a bfloat16 output is
+ *   rounded once, to nearest even.
+ * - stream is a hipStream_t passed as void* (NULL: the null stream).  Work is
+ *   enqueued asynchronously on it; the library never synchronises.  A fault
+ *   inside a kernel surfaces at the caller's next synchronisation.
+ * - Arguments are checked on the host before anything is enqueued: an invalid
+ *   call returns a non-zero gqa_status, touches no memory and enqueues nothing;
+ *   gqa_last_error() then gives a readable reason (per thread).
+ * - Calls that only need host-side checks (an invalid argument, or an empty
+ *   problem, which returns GQA_OK) make no HIP call at all.
+ * - Every call is reentrant: no global state besides the per-thread error
+ *   text.  Calls that share a workspace must not overlap in time.
+ */
+#ifndef GQA_H_
+#define GQA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  GQA_DTYPE_F32 = 0,
+  GQA_DTYPE_BF16 = 1
+};
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARG = 1,   /* shapes, pointers, alignment, scale, H % G != 0   */
+  GQA_ERR_UNSUPPORTED = 2,   /* valid, but not built: head size other than 64/128 */
+  GQA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required        */
+  GQA_ERR_LAUNCH = 4         /* the HIP runtime refused a kernel launch            */
+} gqa_status;
+
+/*
+ * Split planning for gqa_decode.
+ *
+ * A decode call divides each sequence's cache into num_splits slices, runs
+ * one pass per slice and, when num_splits > 1, merges the slices' partial
+ * softmax results (log-sum-exp) in a second pass.  The partial results live in
+ * a caller-provided workspace.
+ *
+ * gqa_decode_num_splits() returns the split count gqa_decode() uses.  It is a
+ * pure function of the shape (it reads no device and no sequence length), so
+ * it and gqa_decode_workspace_bytes() can be called without a GPU.
+ * Returns 0 for an invalid shape.
+ *
+ * gqa_decode_workspace_bytes(): bytes of workspace that a decode of this
+ * shape needs with num_splits slices (num_splits = 0: the planner's choice).
+ * 0 means no workspace is needed.  Returns (size_t)-1 for an invalid shape.
+ */
+int gqa_decode_num_splits(int B, int H, int G, int d, int n_max);
+size_t gqa_decode_workspace_bytes(int B, int H, int G, int d, int n_max, int num_splits);
+
+/*
+ * gqa_decode - one autoregressive decode step of GQA over a K/V cache.
+ *
+ * Defines (the fogdragon CSDN blog on MQA/GQA, section "KV Cache": the new
+ * token's k and v are appended to the cache, then the query attends every
+ * cached position through softmax(logits * scale) and a weighted sum of the
+ * cached values; GQA paper section 2.2 for the head grouping):
+ *
+ *   out[b,h,:] = sum_{j < n_b} softmax_j(scale * q[b,h,:] . K[b,g,j,:]) V[b,g,j,:]
+ *   with g = floor(h * G / H) and n_b = min(seqlens[b], n_max).
+ *
+ *   q        [B, H, d]          dtype, device
+ *   k_cache  [B, G, n_max, d]   dtype, device
+ *   v_cache  [B, G, n_max, d]   dtype, device
+ *   seqlens  [B]                int32, device; the current token's K/V is
+ *                               already at position seqlens[b]-1.  A length of
+ *                               0 (or below) gives a zero output row; lengths
+ *                               above n_max are clamped to n_max.  Cache rows
+ *                               at or beyond the length are never read into
+ *                               arithmetic (they may hold anything, NaN too).
+ *   out      [B, H, d]          dtype, device; written in full.
+ *   scale    finite float, typically 1/sqrt(d).
+ *   d        64 or 128 (anything else: GQA_ERR_UNSUPPORTED).
+ *   workspace/workspace_bytes   device buffer of at least
+ *                               gqa_decode_workspace_bytes(B,H,G,d,n_max,0)
+ *                               bytes; may be NULL/0 when that is 0.  Its
+ *                               contents on entry do not matter.
+ *
+ * Errors: GQA_ERR_INVALID_ARG for B, H, G, n_max < 0 or H, G < 1 with B > 0,
+ * H % G != 0, a NULL or misaligned tensor, an unknown dtype or a non-finite
+ * scale; GQA_ERR_WORKSPACE for a too-small workspace.  B = 0 or n_max = 0 with
+ * B > 0 (then out is zero-filled) are valid.
+ */
+gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seqlens, void* out,
+                      int B, int H, int G, int d, int n_max, float scale, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gqa_decode_split - gqa_decode with an explicit split count (1 .. n_max;
+ * 0 = the planner's choice).  Needs gqa_decode_workspace_bytes(..., num_splits)
+ * bytes of workspace.  Every split count computes the same function; only the
+ * order of the floating-point sums changes.
+ */
+gqa_status gqa_decode_split(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seqlens, void* out,
+                            int B, int H, int G, int d, int n_max, float scale, int dtype,
+                            int num_splits, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * gqa_prefill_causal - causal GQA over whole prompts (the context phase).
+ *
+ * The blog's decoder discussion: the prompt is processed in parallel like an
+ * encoder, but each position only sees itself and earlier positions.  Query
+ * position i of head h attends keys 0..i (inclusive) of K/V head
+ * floor(h * G / H):
+ *
+ *   out[b,i,h,:] = sum_{j <= i} softmax_j(scale * q[b,i,h,:] . k[b,j,g,:]) v[b,j,g,:]
+ *
+ *   q    [B, T, H, d]   dtype, device (token-major)
+ *   k    [B, T, G, d]   dtype, device
+ *   v    [B, T, G, d]   dtype, device
+ *   out  [B, T, H, d]   dtype, device; written in full.
+ *   d    64 or 128.
+ *
+ * bfloat16 runs on the matrix cores (bf16 products, float32 accumulation; the
+ * softmax weights are rounded to bf16 before they multiply V, and the
+ * normaliser sums those rounded weights).  float32 runs on the vector units
+ * in float32.  Errors as for gqa_decode; B = 0 or T = 0 is a valid no-op.
+ */
+gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void* out,
+                              int B, int T, int H, int G, int d, float scale, int dtype,
+                              void* stream);
+
+/*
+ * kv_meanpool_heads - MHA -> GQA checkpoint conversion of one projection.
+ *
+ * GQA paper section 2.1 (Figure 1) and section 2.2; tutorial section 4.3,
+ * step 2: each group's key (or value) projection is the mean of the
+ * projections of the heads in that group.  Call it once for the key weights
+ * and once for the value weights.
+ *
+ *   w_in   [H, per_head_elems]   dtype, device: head h's weights, contiguous
+ *                                (e.g. a [d_model, d_head] matrix per head)
+ *   w_out  [G, per_head_elems]   dtype, device:
+ *          w_out[g, e] = (sum_{k < n_rep} w_in[g*n_rep + k, e]) / n_rep
+ *          summed in float32, divided once (correctly rounded) and rounded
+ *          once to dtype.
+ *
+ * Errors: GQA_ERR_INVALID_ARG for H, G < 1, H % G != 0, per_head_elems < 0,
+ * NULL/misaligned pointers (with per_head_elems > 0) or an unknown dtype.
+ * per_head_elems = 0 is a valid no-op.
+ */
+gqa_status kv_meanpool_heads(const void* w_in, void* w_out, int H, int G,
+                             int64_t per_head_elems, int dtype, void* stream);
+
+/* Static text for a status code ("GQA_OK", ...); never NULL. */
+const char* gqa_status_string(int status);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* gqa_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int gqa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H_ */

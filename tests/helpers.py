@@ -1,0 +1,51 @@
+"""Shared helpers for the GPU parity tests (comparison against the float64 oracle)."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+# Tolerances for GPU vs float64 oracle on the same (rounded) inputs.
+F32_MAX_ABS = 1e-5
+BF16_MAX_ABS = 1.5e-2
+BF16_MEAN_ABS = 2e-3
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def announce(msg: str) -> None:
+    """Name the case on stdout before a GPU step (so a crash still says what ran)."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
+
+
+def assert_close(got: torch.Tensor, ref: np.ndarray, dtype: torch.dtype, what: str = "") -> dict:
+    g = to64(got)
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    err = np.abs(g - ref)
+    stats = {"max_abs": float(err.max(initial=0.0)), "mean_abs": float(err.mean()) if err.size else 0.0}
+    if dtype == torch.float32:
+        assert stats["max_abs"] <= F32_MAX_ABS, f"{what}: {stats}"
+    else:
+        assert stats["max_abs"] <= BF16_MAX_ABS and stats["mean_abs"] <= BF16_MEAN_ABS, f"{what}: {stats}"
+    return stats
+
+
+def bf16_ulp_distance(got_bf16: torch.Tensor, ref: np.ndarray) -> np.ndarray:
+    """|bits(got) - bits(RNE_bf16(ref))| as integers (same-sign values assumed near)."""
+    want = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16)
+    a = got_bf16.detach().cpu().view(torch.int16).numpy().astype(np.int64)
+    b = want.view(torch.int16).numpy().astype(np.int64)
+    # map sign-magnitude to a monotone integer line
+    a = np.where(a < 0, -(a & 0x7FFF), a)
+    b = np.where(b < 0, -(b & 0x7FFF), b)
+    return np.abs(a - b)

@@ -1,0 +1,157 @@
+"""Host-side checks of libgqa.so's C ABI.  No GPU: every call here returns before
+the library makes any HIP call (argument checks, empty problems, planning)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import grouped_query_decode_amd as gqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+F32, BF16 = 0, 1
+P = ctypes.c_void_p(4096)        # aligned, non-null, never dereferenced on these paths
+P_MIS = ctypes.c_void_p(4100)    # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gqa.library_path()):
+        pytest.fail("libgqa.so is not built: run __graft_entry__.build() first")
+    return gqa.load_library()
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    for n in ("gqa_decode", "gqa_decode_split", "gqa_prefill_causal", "kv_meanpool_heads",
+              "gqa_decode_workspace_bytes", "gqa_decode_num_splits", "gqa_status_string",
+              "gqa_last_error", "gqa_version"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(gqa.library_path())
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} declared in include/gqa.h but not exported"
+
+
+def test_status_strings(lib):
+    assert lib.gqa_status_string(0) == b"GQA_OK"
+    assert lib.gqa_status_string(1) == b"GQA_ERR_INVALID_ARG"
+    assert lib.gqa_status_string(3) == b"GQA_ERR_WORKSPACE"
+    assert lib.gqa_status_string(99) == b"GQA_ERR_UNKNOWN"
+    assert lib.gqa_version() >= 100
+
+
+def _decode(lib, q=P, k=P, v=P, sl=P, out=P, B=2, H=8, G=2, d=64, n=128, scale=0.125, dt=BF16,
+            splits=0, ws=None, ws_bytes=0):
+    return lib.gqa_decode_split(q, k, v, sl, out, B, H, G, d, n, scale, dt, splits,
+                                ws if ws is not None else ctypes.c_void_p(0), ws_bytes, None)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    assert _decode(lib, H=6, G=4) == INVALID
+    assert "multiple" in lib.gqa_last_error().decode()
+    assert _decode(lib, G=0) == INVALID
+    assert _decode(lib, B=-1) == INVALID
+    assert _decode(lib, n=-5) == INVALID
+    assert _decode(lib, dt=7) == INVALID
+    assert _decode(lib, scale=float("nan")) == INVALID
+    assert _decode(lib, scale=float("inf")) == INVALID
+    assert _decode(lib, q=ctypes.c_void_p(0)) == INVALID
+    assert _decode(lib, sl=ctypes.c_void_p(0)) == INVALID
+    assert _decode(lib, k=P_MIS) == INVALID
+    assert "aligned" in lib.gqa_last_error().decode()
+    assert _decode(lib, splits=-1) == INVALID
+    assert _decode(lib, d=96) == UNSUPPORTED
+    assert _decode(lib, d=256) == UNSUPPORTED
+
+
+def test_decode_empty_batch_is_a_noop(lib):
+    # B = 0: valid, nothing to do, no pointer is looked at
+    z = ctypes.c_void_p(0)
+    assert _decode(lib, q=z, k=z, v=z, sl=z, out=z, B=0) == OK
+    assert lib.gqa_last_error() == b""
+
+
+def test_decode_workspace_checked_before_launch(lib):
+    need = lib.gqa_decode_workspace_bytes(16, 32, 8, 128, 1024, 0)
+    assert need > 0
+    assert _decode(lib, B=16, H=32, G=8, d=128, n=1024) == WORKSPACE
+    assert _decode(lib, B=16, H=32, G=8, d=128, n=1024, ws=P, ws_bytes=need - 1) == WORKSPACE
+    assert _decode(lib, B=16, H=32, G=8, d=128, n=1024, ws=P_MIS, ws_bytes=need) == WORKSPACE
+
+
+def test_split_planner_is_host_only_and_consistent(lib):
+    shapes = [(1, 8, 2, 64, 128), (16, 32, 32, 128, 1024), (16, 32, 8, 128, 1024),
+              (16, 32, 1, 128, 1024), (32, 64, 8, 64, 2048), (64, 32, 8, 128, 32768)]
+    for B, H, G, d, n in shapes:
+        S = lib.gqa_decode_num_splits(B, H, G, d, n)
+        assert 1 <= S <= max(1, n)
+        ws = lib.gqa_decode_workspace_bytes(B, H, G, d, n, 0)
+        if S == 1:
+            assert ws == 0
+        else:
+            o_bytes = B * H * S * d * 4
+            assert ws == (o_bytes + 255) // 256 * 256 + B * H * S * 2 * 4
+        assert ws == lib.gqa_decode_workspace_bytes(B, H, G, d, n, S)
+    # long ragged caches are cut into bounded slices
+    assert lib.gqa_decode_num_splits(64, 32, 8, 128, 32768) >= 16
+    # forced split counts
+    assert lib.gqa_decode_workspace_bytes(1, 8, 2, 64, 128, 1) == 0
+    assert lib.gqa_decode_workspace_bytes(1, 8, 2, 64, 128, 7) > 0
+    # invalid shapes
+    assert lib.gqa_decode_num_splits(1, 6, 4, 64, 128) == 0
+    assert lib.gqa_decode_workspace_bytes(1, 6, 4, 64, 128, 0) == ctypes.c_size_t(-1).value
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    def call(q=P, k=P, v=P, out=P, B=2, T=64, H=8, G=2, d=128, scale=0.1, dt=BF16):
+        return lib.gqa_prefill_causal(q, k, v, out, B, T, H, G, d, scale, dt, None)
+    assert call(H=8, G=3) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(v=ctypes.c_void_p(0)) == INVALID
+    assert call(out=P_MIS) == INVALID
+    assert call(scale=float("-inf")) == INVALID
+    assert call(d=80) == UNSUPPORTED
+    z = ctypes.c_void_p(0)
+    assert call(q=z, k=z, v=z, out=z, T=0) == OK
+    assert call(q=z, k=z, v=z, out=z, B=0) == OK
+
+
+def test_meanpool_rejects_bad_arguments(lib):
+    def call(w=P, o=P, H=64, G=8, n=4096 * 64, dt=BF16):
+        return lib.kv_meanpool_heads(w, o, H, G, n, dt, None)
+    assert call(G=3) == INVALID
+    assert call(G=0) == INVALID
+    assert call(n=-1) == INVALID
+    assert call(w=ctypes.c_void_p(0)) == INVALID
+    assert call(o=P_MIS) == INVALID
+    assert call(dt=5) == INVALID
+    assert call(w=ctypes.c_void_p(0), o=ctypes.c_void_p(0), n=0) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(gqa, "_lib", None)
+    monkeypatch.setattr(gqa, "_PKG_DIR", str(tmp_path))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        gqa.load_library()
+
+
+def test_binding_rejects_host_tensors(lib):
+    import torch
+    q = torch.zeros(1, 8, 64)
+    k = torch.zeros(1, 2, 16, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        gqa.decode(q, k, k, torch.zeros(1, dtype=torch.int32))

@@ -1,0 +1,282 @@
+"""GPU parity of gqa_decode against the float64 oracle (through the C ABI binding)."""
+
+import numpy as np
+import pytest
+import torch
+
+import grouped_query_decode_amd as gqa
+import oracle
+import synth
+from helpers import announce, assert_close, need_gpu, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    gqa.load_library()
+
+
+def _run(x, scale, num_splits=0, out=None):
+    o = gqa.decode(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=scale, out=out,
+                   num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o
+
+
+def _oracle(x, scale, rows=None):
+    sl = x["seqlens"].cpu().numpy()
+    if rows is None:
+        return oracle.decode_ref(to64(x["q"]), to64(x["k_cache"]), to64(x["v_cache"]), sl, scale)
+    # only the listed sequences, copying just their attended cache rows
+    outs = []
+    for b in rows:
+        n = oracle.attended_length(sl[b], x["k_cache"].shape[2])
+        n = max(n, 1)
+        q = to64(x["q"][b:b + 1])
+        k = to64(x["k_cache"][b:b + 1, :, :n])
+        v = to64(x["v_cache"][b:b + 1, :, :n])
+        outs.append(oracle.decode_ref(q, k, v, [sl[b]], scale)[0])
+    return np.stack(outs)
+
+
+# ---------------------------------------------------------------------------
+# the tiny float32 workload: 8 heads, G = 2 (GQA), 8 (MHA), 1 (MQA)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G", [2, 8, 1])
+def test_tiny_f32_group_sweep(G):
+    w = synth.WORKLOADS["tiny_decode_f32"]
+    announce(f"decode tiny f32 G={G}")
+    x = synth.decode_inputs(w.B, w.H, G, w.d, w.N, dtype="f32", seed=w.seed, device=DEV)
+    scale = synth.scale_for(w.d)
+    assert_close(_run(x, scale), _oracle(x, scale), torch.float32, f"tiny G={G}")
+
+
+def test_tiny_f32_repeat_kv_reproduces_gqa():
+    announce("decode tiny f32 repeat_kv")
+    x = synth.decode_inputs(1, 8, 2, 64, 128, dtype="f32", seed=0, device=DEV)
+    scale = synth.scale_for(64)
+    a = _run(x, scale)
+    xr = dict(x)
+    xr["k_cache"] = x["k_cache"].repeat_interleave(4, dim=1).contiguous()
+    xr["v_cache"] = x["v_cache"].repeat_interleave(4, dim=1).contiguous()
+    b = _run(xr, scale)
+    assert (a - b).abs().max().item() <= 1e-6
+
+
+# ---------------------------------------------------------------------------
+# shapes that span several tiles, ragged tails, every group size
+# ---------------------------------------------------------------------------
+
+CASES = [
+    # B, H, G, d, Nmax, dtype
+    (3, 8, 2, 64, 300, "bf16"),
+    (2, 32, 8, 128, 777, "bf16"),
+    (2, 32, 32, 128, 129, "bf16"),
+    (2, 32, 1, 128, 200, "bf16"),
+    (2, 64, 8, 64, 450, "bf16"),
+    (2, 16, 16, 64, 97, "bf16"),
+    (2, 32, 2, 128, 160, "bf16"),
+    (2, 64, 2, 64, 130, "bf16"),      # n_rep = 32
+    (2, 24, 8, 128, 140, "bf16"),     # n_rep = 3
+    (3, 8, 2, 128, 300, "f32"),
+    (2, 32, 4, 64, 260, "f32"),
+    (2, 32, 1, 64, 100, "f32"),       # n_rep = 32 on the vector units
+]
+
+
+@pytest.mark.parametrize("B,H,G,d,n_max,dt", CASES)
+def test_decode_ragged_cases(B, H, G, d, n_max, dt):
+    announce(f"decode B={B} H={H} G={G} d={d} Nmax={n_max} {dt}")
+    rng = np.random.default_rng(B * 1000 + H + G + d + n_max)
+    lens = [int(rng.integers(1, n_max + 1)) for _ in range(B)]
+    lens[0] = n_max
+    if B > 2:
+        lens[2] = 1
+    x = synth.decode_inputs(B, H, G, d, n_max, dtype=dt, seed=7, device=DEV, seqlens=lens,
+                            nan_tail=True)
+    scale = synth.scale_for(d)
+    assert_close(_run(x, scale), _oracle(x, scale), x["q"].dtype, "ragged")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("S", [1, 2, 7, 64, 1000])
+def test_forced_split_counts(dt, S):
+    announce(f"decode forced splits S={S} {dt}")
+    x = synth.decode_inputs(3, 16, 4, 128, 1000, dtype=dt, seed=3, device=DEV,
+                            seqlens=[1000, 513, 31], nan_tail=True)
+    scale = synth.scale_for(128)
+    assert_close(_run(x, scale, num_splits=S), _oracle(x, scale), x["q"].dtype, f"S={S}")
+
+
+def test_lengths_zero_and_beyond_capacity():
+    announce("decode seqlen 0 and > Nmax")
+    x = synth.decode_inputs(4, 8, 2, 64, 96, dtype="bf16", seed=4, device=DEV,
+                            seqlens=[0, 96, 500, -3])
+    scale = 0.125
+    out = _run(x, scale).clone()
+    ref = _oracle(x, scale)
+    assert torch.equal(out[0], torch.zeros_like(out[0]))
+    assert torch.equal(out[3], torch.zeros_like(out[3]))
+    assert_close(out, ref, torch.bfloat16, "lengths")
+    # a length of 500 behaves exactly like the capacity 96
+    x2 = dict(x)
+    x2["seqlens"] = torch.tensor([0, 96, 96, 0], dtype=torch.int32, device=DEV)
+    out2 = _run(x2, scale)
+    assert torch.equal(out, out2)
+
+
+def test_empty_cache_capacity_gives_zeros():
+    announce("decode Nmax = 0")
+    q = torch.randn(2, 8, 64, device=DEV).to(torch.bfloat16)
+    k = torch.empty(2, 2, 0, 64, device=DEV, dtype=torch.bfloat16)
+    out = torch.full_like(q, 3.0)
+    gqa.decode(q, k, k, torch.tensor([0, 5], dtype=torch.int32, device=DEV), out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, torch.zeros_like(out))
+
+
+# ---------------------------------------------------------------------------
+# bit-exact properties
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_masking_is_bit_exact(dt):
+    """Cache rows at or beyond the length cannot change a single output bit."""
+    announce(f"decode masking bits {dt}")
+    B, H, G, d, n_max = 4, 32, 8, 128, 700
+    lens = [700, 333, 64, 1]
+    base = synth.decode_inputs(B, H, G, d, n_max, dtype=dt, seed=11, device=DEV, seqlens=lens)
+    scale = synth.scale_for(d)
+    outs = []
+    for fill in ("nan", "random", "dominant"):
+        x = {k: v.clone() for k, v in base.items()}
+        for b, n in enumerate(lens):
+            if fill == "nan":
+                x["k_cache"][b, :, n:] = float("nan")
+                x["v_cache"][b, :, n:] = float("nan")
+            elif fill == "random":
+                x["k_cache"][b, :, n:] = torch.randn_like(x["k_cache"][b, :, n:].float()).to(x["k_cache"].dtype)
+                x["v_cache"][b, :, n:] = 1e4
+            else:
+                if n < n_max:
+                    qg = x["q"][b].float().view(G, H // G, d).sum(1)
+                    x["k_cache"][b, :, n] = (qg * 100).to(x["k_cache"].dtype)
+                    x["v_cache"][b, :, n] = 1e4
+        outs.append(_run(x, scale).clone())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    # the last attended position does count: a dominant key there takes over
+    x = {k: v.clone() for k, v in base.items()}
+    for b, n in enumerate(lens):
+        qg = x["q"][b].float().view(G, H // G, d).sum(1)
+        x["k_cache"][b, :, n - 1] = (qg * 100).to(x["k_cache"].dtype)
+        x["v_cache"][b, :, n - 1] = 2.0
+    out = _run(x, scale)
+    assert torch.equal(out, torch.full_like(out, 2.0))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("H,G", [(32, 8), (8, 2), (64, 64), (32, 1), (24, 8)])
+def test_group_map_is_bit_exact(dt, H, G):
+    """V of K/V head g is a distinct power of two: every output element names its group.
+
+    bfloat16 outputs equal the constant exactly; float32 outputs carry the
+    normaliser's rounding, so there the nearest constant must be the right one.
+    """
+    announce(f"decode group map H={H} G={G} {dt}")
+    B, d, n_max = 2, 64 if H == 64 else 128, 200
+    x = synth.decode_inputs(B, H, G, d, n_max, dtype=dt, seed=5, device=DEV, seqlens=[200, 77])
+    for perm in (list(range(G)), list(reversed(range(G)))):
+        consts = torch.tensor([2.0 ** (gg - G // 2) for gg in perm], dtype=torch.float64)
+        x["v_cache"] = consts.view(1, G, 1, 1).expand(B, G, n_max, d).to(DEV).to(x["k_cache"].dtype).contiguous()
+        out = _run(x, synth.scale_for(d)).double().cpu()
+        want_g = torch.tensor([oracle.kv_group_of_head(h, H, G) for h in range(H)])
+        want = consts[want_g].view(1, H, 1).expand(B, H, d)
+        if dt == "bf16":
+            assert torch.equal(out, want)
+        else:
+            nearest = (out[..., None].log2() - consts.log2().view(1, 1, 1, G)).abs().argmin(-1)
+            assert torch.equal(nearest, want_g.view(1, H, 1).expand(B, H, d))
+            assert ((out - want).abs() / want).max().item() <= 1e-6
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_single_key_returns_its_value(dt):
+    announce(f"decode single key {dt}")
+    B, H, G, d = 3, 32, 8, 128
+    x = synth.decode_inputs(B, H, G, d, 64, dtype=dt, seed=6, device=DEV, seqlens=[1, 1, 1])
+    x["q"] = (x["q"].float() * 30).to(x["q"].dtype)
+    out = _run(x, synth.scale_for(d))
+    want = x["v_cache"][:, :, 0].repeat_interleave(H // G, dim=1)
+    assert torch.equal(out, want)
+
+
+def test_constant_values_are_exact_bf16():
+    announce("decode constant V bf16")
+    B, H, G, d, n = 2, 32, 4, 128, 999
+    x = synth.decode_inputs(B, H, G, d, n, dtype="bf16", seed=8, device=DEV)
+    x["v_cache"] = torch.full_like(x["v_cache"], 0.375)
+    out = _run(x, synth.scale_for(d))
+    assert torch.equal(out, torch.full_like(out, 0.375))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_deterministic(dt):
+    announce(f"decode determinism {dt}")
+    x = synth.decode_inputs(8, 32, 8, 128, 3000, dtype=dt, seed=9, device=DEV, seqlens="uniform")
+    a = _run(x, 0.1).clone()
+    b = _run(x, 0.1)
+    assert torch.equal(a, b)
+
+
+def test_output_guard_untouched():
+    announce("decode guard canaries")
+    B, H, G, d, n = 2, 32, 8, 128, 1024
+    x = synth.decode_inputs(B, H, G, d, n, dtype="bf16", seed=10, device=DEV)
+    pad = 4096
+    buf = torch.full((pad + B * H * d + pad,), 7.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[pad:pad + B * H * d].view(B, H, d)
+    _run(x, synth.scale_for(d), out=out)
+    assert torch.equal(buf[:pad], torch.full((pad,), 7.0, dtype=torch.bfloat16, device=DEV))
+    assert torch.equal(buf[-pad:], torch.full((pad,), 7.0, dtype=torch.bfloat16, device=DEV))
+    assert_close(out, _oracle(x, synth.scale_for(d)), torch.bfloat16, "guard")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G", [32, 8, 4, 1])
+def test_llama7b_decode_group_sweep(G):
+    w = synth.WORKLOADS["llama7b_decode_bf16"]
+    announce(f"decode llama7b G={G}")
+    x = synth.decode_inputs(w.B, w.H, G, w.d, w.N, dtype="bf16", seed=w.seed, device=DEV)
+    scale = synth.scale_for(w.d)
+    assert_close(_run(x, scale), _oracle(x, scale), torch.bfloat16, f"llama7b G={G}")
+
+
+def test_t5xxl_cross_attention_decode():
+    w = synth.WORKLOADS["t5xxl_cross_decode_bf16"]
+    announce("decode t5xxl cross")
+    x = synth.decode_inputs(w.B, w.H, w.G, w.d, w.N, dtype="bf16", seed=w.seed, device=DEV)
+    scale = synth.scale_for(w.d)
+    assert_close(_run(x, scale), _oracle(x, scale), torch.bfloat16, "t5xxl")
+
+
+def test_ragged_long_context_decode():
+    w = synth.WORKLOADS["ragged_longctx_decode_bf16"]
+    announce("decode ragged long context (8 GiB cache)")
+    x = synth.decode_inputs(w.B, w.H, w.G, w.d, w.N, dtype="bf16", seed=w.seed, device=DEV,
+                            seqlens="uniform", nan_tail=True)
+    scale = synth.scale_for(w.d)
+    out = _run(x, scale)
+    assert torch.isfinite(out.float()).all()
+    sl = x["seqlens"].cpu().numpy()
+    rows = sorted({int(np.argmin(sl)), int(np.argmax(sl)), 0, 17, 33, 63})
+    ref = _oracle(x, scale, rows=rows)
+    assert_close(out[rows], ref, torch.bfloat16, "ragged long")
+    del x
+    torch.cuda.empty_cache()

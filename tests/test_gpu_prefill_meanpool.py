@@ -1,0 +1,140 @@
+"""GPU parity of gqa_prefill_causal and kv_meanpool_heads against the float64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import grouped_query_decode_amd as gqa
+import oracle
+import synth
+from helpers import announce, assert_close, bf16_ulp_distance, need_gpu, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    gqa.load_library()
+
+
+def _prefill(x, scale):
+    o = gqa.prefill_causal(x["q"], x["k"], x["v"], scale=scale)
+    torch.cuda.synchronize()
+    return o
+
+
+PREFILL_CASES = [
+    # B, T, H, G, d, dtype
+    (2, 200, 8, 2, 128, "bf16"),
+    (1, 333, 32, 8, 128, "bf16"),
+    (2, 130, 8, 8, 64, "bf16"),      # n_rep = 1
+    (2, 97, 8, 4, 64, "bf16"),       # n_rep = 2
+    (1, 150, 32, 1, 128, "bf16"),    # n_rep = 32
+    (1, 64, 24, 8, 128, "bf16"),     # n_rep = 3 (vector units)
+    (1, 1, 8, 2, 128, "bf16"),       # single position
+    (2, 100, 8, 2, 64, "f32"),
+    (1, 70, 16, 16, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,T,H,G,d,dt", PREFILL_CASES)
+def test_prefill_cases(B, T, H, G, d, dt):
+    announce(f"prefill B={B} T={T} H={H} G={G} d={d} {dt}")
+    x = synth.prefill_inputs(B, T, H, G, d, dtype=dt, seed=T + H, device=DEV, std=0.5)
+    scale = synth.scale_for(d)
+    out = _prefill(x, scale)
+    ref = oracle.prefill_causal_ref(to64(x["q"]), to64(x["k"]), to64(x["v"]), scale)
+    assert_close(out, ref, x["q"].dtype, "prefill")
+    # row 0 attends only key 0: exactly its value
+    want0 = x["v"][:, 0].repeat_interleave(H // G, dim=1)
+    assert torch.equal(out[:, 0], want0)
+
+
+def test_prefill_row_matches_decode():
+    """Prefill row i equals a decode step over the first i+1 positions."""
+    announce("prefill vs decode rows")
+    B, T, H, G, d = 2, 300, 32, 8, 128
+    x = synth.prefill_inputs(B, T, H, G, d, dtype="bf16", seed=3, device=DEV)
+    scale = synth.scale_for(d)
+    out = _prefill(x, scale)
+    kc = x["k"].transpose(1, 2).contiguous()
+    vc = x["v"].transpose(1, 2).contiguous()
+    for i in (0, 1, 63, 64, 65, 127, 128, 299):
+        dec = gqa.decode(x["q"][:, i].contiguous(), kc, vc,
+                         torch.full((B,), i + 1, dtype=torch.int32, device=DEV), scale=scale)
+        torch.cuda.synchronize()
+        diff = (out[:, i].float() - dec.float()).abs().max().item()
+        assert diff <= 1.6e-2, (i, diff)
+
+
+def test_prefill_deterministic():
+    announce("prefill determinism")
+    x = synth.prefill_inputs(1, 512, 32, 8, 128, dtype="bf16", seed=4, device=DEV)
+    a = _prefill(x, 0.09).clone()
+    b = _prefill(x, 0.09)
+    assert torch.equal(a, b)
+
+
+def test_causal_prefill_full_size_sampled_rows():
+    w = synth.WORKLOADS["causal_prefill_bf16"]
+    announce("prefill full size B=2 T=4096 H=32 G=8 d=128")
+    x = synth.prefill_inputs(w.B, w.N, w.H, w.G, w.d, dtype="bf16", seed=w.seed, device=DEV,
+                             std=w.std)
+    scale = synth.scale_for(w.d)
+    out = _prefill(x, scale)
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(0)
+    rows = sorted({0, 1, 31, 32, 63, 64, 127, 2047, 2048, 4094, 4095,
+                   *rng.integers(0, w.N, size=24).tolist()})
+    ref = oracle.prefill_causal_ref(to64(x["q"]), to64(x["k"]), to64(x["v"]), scale, rows=rows)
+    assert_close(out[:, rows], ref[:, rows], torch.bfloat16, "prefill full")
+
+
+# ---------------------------------------------------------------------------
+# kv_meanpool_heads
+# ---------------------------------------------------------------------------
+
+def _meanpool(w, G):
+    o = gqa.meanpool_heads(w, G)
+    torch.cuda.synchronize()
+    return o
+
+
+def test_meanpool_t5xxl_projection_bf16():
+    wl = synth.WORKLOADS["t5xxl_meanpool_bf16"]
+    announce("meanpool [64,4096,64] -> 8 bf16")
+    for seed in (0, 1):          # one call for the K weights, one for the V weights
+        w = synth.meanpool_inputs(wl.H, wl.per_head_shape, dtype="bf16", seed=seed, device=DEV)["w"]
+        out = _meanpool(w, wl.G)
+        ref = oracle.meanpool_ref(to64(w), wl.G)
+        ulps = bf16_ulp_distance(out, ref)
+        assert ulps.max() <= 1, ulps.max()
+        exact = float((ulps == 0).mean())
+        assert exact >= 0.99, exact
+
+
+@pytest.mark.parametrize("H,G,shape,dt", [
+    (8, 2, (16, 64), "f32"), (8, 8, (5, 3), "bf16"), (6, 3, (7, 5), "bf16"),
+    (6, 1, (33,), "f32"), (64, 8, (4096, 64), "f32"), (32, 4, (13, 8), "bf16"),
+])
+def test_meanpool_cases(H, G, shape, dt):
+    announce(f"meanpool H={H} G={G} shape={shape} {dt}")
+    w = synth.meanpool_inputs(H, shape, dtype=dt, seed=H + G, device=DEV)["w"]
+    out = _meanpool(w, G)
+    ref = oracle.meanpool_ref(to64(w), G)
+    if dt == "f32":
+        assert np.abs(to64(out) - ref).max() <= 1e-5
+    else:
+        assert bf16_ulp_distance(out, ref).max() <= 1
+    if G == H:
+        assert torch.equal(out, w)
+
+
+def test_meanpool_identical_heads_bit_exact():
+    announce("meanpool identical heads")
+    base = synth.meanpool_inputs(1, (512, 64), dtype="bf16", seed=3, device=DEV)["w"]
+    w = base.expand(16, 512, 64).contiguous()
+    out = _meanpool(w, 4)
+    assert torch.equal(out, base.expand(4, 512, 64))
