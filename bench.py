@@ -110,8 +110,8 @@ def bench_decode(torch, gqa, synth, name, G, steps, warmup, replicas_bytes=1 << 
                                 seqlens=w.seqlens, nan_tail=w.nan_tail) for r in range(R)]
     q = reps[0]["q"]
     out = torch.empty_like(q)
-    ws_n = gqa.decode_workspace_bytes(B, H, G, d, N)
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+    # zero-filled once; the library leaves its counter header zero after each call
+    ws = torch.zeros(max(gqa.decode_workspace_bytes(B, H, G, d, N), 1), dtype=torch.uint8, device=dev)
     scale = synth.scale_for(d)
 
     def call(i):
@@ -174,6 +174,17 @@ def bench_meanpool(torch, gqa, synth, steps, warmup):
     return {"H": w.H, "G": w.G, "per_head_shape": list(w.per_head_shape), "replicas": R,
             "ms_per_call": round(ms, 6), "bytes_per_call": nbytes, "GBps": round(gbps, 1),
             "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def bench_read_probe(torch, steps):
+    """Sum of a 2 GiB bf16 tensor (PyTorch's reduction): an achievable-read-bandwidth reference."""
+    a = torch.ones(1 << 30, dtype=torch.bfloat16, device="cuda:0")
+    ms = _time_calls(torch, lambda i: a.sum(dtype=torch.float32), max(5, steps // 10), 3)
+    moved = a.numel() * a.element_size()
+    del a
+    torch.cuda.empty_cache()
+    return {"bytes_per_call": moved, "ms_per_call": round(ms, 6),
+            "GBps": round(moved / (ms * 1e-3) / 1e9, 1)}
 
 
 def bench_copy_probe(torch, steps):
@@ -264,11 +275,12 @@ def main():
         secondary["causal_prefill"] = bench_prefill(torch, gqa, synth, max(20, args.steps // 5), 3)
         secondary["t5xxl_meanpool"] = bench_meanpool(torch, gqa, synth, args.steps, args.warmup)
         secondary["hbm_copy_probe"] = bench_copy_probe(torch, args.steps)
+        secondary["hbm_read_probe"] = bench_read_probe(torch, args.steps)
 
     traffic = stored_traffic()
     roofline = {"bound": "hbm", "achieved": head["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(head["GBps"] / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "decode_mfma_kernel<128,1> (+ split combine)",
+                "kernel": "decode_mfma_kernel<128,1> (split merge fused)",
                 "algorithmic_bytes_per_launch": head["bytes_per_call"]}
     line = {
         "metric": METRIC,

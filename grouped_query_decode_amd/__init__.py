@@ -27,6 +27,7 @@ __all__ = [
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libgqa.so"
 _lib = None
+_workspaces: dict = {}
 
 DTYPE_CODES = {torch.float32: 0, torch.bfloat16: 1}
 
@@ -121,6 +122,16 @@ def decode_workspace_bytes(B: int, H: int, G: int, d: int, n_max: int, num_split
     return int(n)
 
 
+def _cached_workspace(dev, need: int) -> torch.Tensor:
+    """A zero-filled workspace per device, grown on demand (the library keeps its
+    counter header zero between calls, so it is cleared only when allocated)."""
+    t = _workspaces.get(dev)
+    if t is None or t.numel() < need:
+        t = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=dev)
+        _workspaces[dev] = t
+    return t
+
+
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlens: torch.Tensor,
            scale: float | None = None, out: torch.Tensor | None = None,
            workspace: torch.Tensor | None = None, num_splits: int = 0) -> torch.Tensor:
@@ -128,7 +139,10 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlen
 
     q [B,H,d]; k_cache, v_cache [B,G,Nmax,d]; seqlens [B] int32 (on the GPU).
     ``scale`` defaults to 1/sqrt(d) (as a float32 value).  ``num_splits`` = 0
-    lets the library plan the split-N decomposition.
+    lets the library plan the split-N decomposition.  Without ``workspace`` a
+    zero-filled buffer cached per device is used (shared by all calls on that
+    device: calls on different streams that may overlap should each pass
+    their own, zero-filled once).
     """
     lib = load_library()
     if q.dim() != 3 or k_cache.dim() != 4:
@@ -154,8 +168,8 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlen
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = decode_workspace_bytes(B, H, G, d, n_max, num_splits) if B > 0 else 0
-    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if need > 0 and workspace is None:
+        workspace = _cached_workspace(dev, need)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.gqa_decode_split(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(out),
                               B, H, G, d, n_max, float(scale), _dtype_code(q), int(num_splits),

@@ -35,12 +35,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Split planning.  The decode kernels run one workgroup per (sequence,
-// K/V head, split).  Enough workgroups are wanted to keep all 256 compute
-// units streaming (a few resident per CU), but each split should be long
-// enough that its partial result (d + 2 floats per head, written and read
-// back once) stays small next to the K/V bytes it covers.  Long caches are cut
-// into bounded slices so that ragged lengths balance across the machine.
-constexpr int64_t kTargetWorkgroups = 1024;
+// K/V head, split).  About two workgroups per compute unit (512 on the 256
+// CUs) are wanted so that every CU streams its share of the cache at once;
+// splits are whole 32-position tiles, at least 128 positions (one tile for each
+// of a workgroup's four waves), which also bounds the merge work of the last
+// workgroup.  Long caches are cut into slices of at
+// most 2048 positions so that ragged lengths balance across the machine.  The
+// partial result of a split (d + 2 floats per head, written and read back
+// once) stays small next to the K/V bytes it covers.
+constexpr int64_t kTargetWorkgroups = 512;
 constexpr int64_t kMinSplitLen = 128;
 constexpr int64_t kMaxSplitLen = 2048;
 
@@ -76,12 +79,23 @@ void split_geometry(int n_max, int S, int* S_used, int* split_len) {
   *S_used = int(ceil_div(n_max, len));
 }
 
+// Workspace layout (only when S > 1):
+//   [0, 64 KiB)              split-arrival counters, one int per (b, g); every
+//                            completed call leaves them zero
+//   [64 KiB, +o_bytes)       partial outputs, float [B, H, S, d]
+//   [.., +ml_bytes)          partial (max, sum), float [B, H, S, 2]
+constexpr size_t kCounterBytes = 65536;
+constexpr int64_t kMaxCountedUnits = int64_t(kCounterBytes / sizeof(int));
+
+size_t partial_o_bytes(int B, int H, int d, int S) {
+  return size_t(B) * size_t(H) * size_t(S) * size_t(d) * sizeof(float);
+}
+
 size_t workspace_for(int B, int H, int d, int S) {
   if (S <= 1 || B <= 0) return 0;
-  const size_t rows = size_t(B) * size_t(H) * size_t(S);
-  const size_t o_bytes = rows * size_t(d) * sizeof(float);
-  const size_t ml_bytes = rows * 2 * sizeof(float);
-  return ((o_bytes + 255) / 256) * 256 + ml_bytes;
+  const size_t o_bytes = partial_o_bytes(B, H, d, S);
+  const size_t ml_bytes = size_t(B) * size_t(H) * size_t(S) * 2 * sizeof(float);
+  return kCounterBytes + ((o_bytes + 255) / 256) * 256 + ml_bytes;
 }
 
 gqa_status launched(hipError_t e, const char* what) {
@@ -127,10 +141,13 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
 
   float* part_o = nullptr;
   float* part_ml = nullptr;
+  int* counters = nullptr;
   if (need > 0) {
-    part_o = static_cast<float*>(ws);
-    const size_t o_bytes = size_t(B) * H * S * d * sizeof(float);
-    part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ((o_bytes + 255) / 256) * 256);
+    char* base = static_cast<char*>(ws);
+    counters = reinterpret_cast<int*>(base);
+    part_o = reinterpret_cast<float*>(base + kCounterBytes);
+    const size_t o_bytes = partial_o_bytes(B, H, d, S);
+    part_ml = reinterpret_cast<float*>(base + kCounterBytes + ((o_bytes + 255) / 256) * 256);
   }
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
   const int n_rep = H / G;
@@ -144,12 +161,14 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
     p.out = static_cast<uint16_t*>(out);
     p.part_o = part_o;
     p.part_ml = part_ml;
+    // the split merge runs inside the decode kernel when the counters fit
+    p.counters = (S > 1 && int64_t(B) * G <= kMaxCountedUnits) ? counters : nullptr;
     p.B = B; p.H = H; p.G = G; p.n_rep = n_rep; p.d = d; p.n_max = n_max;
     p.scale = scale;
     p.num_splits = S;
     p.split_len = split_len;
     gqa_status st = launched(gqa::launch_decode_mfma(p, stream), "gqa_decode");
-    if (st != GQA_OK) return st;
+    if (st != GQA_OK || S == 1 || p.counters != nullptr) return st;
   } else {
     gqa::RowsProblem p{};
     p.q = q; p.k = k; p.v = v; p.seqlens = seqlens; p.out = out;

@@ -4,10 +4,10 @@
 // softmax(scale * q.K) over the cached positions and a weighted sum of V);
 // GQA paper section 2.2 (n_rep = H/G query heads share one K/V head).
 //
-// Work unit: one workgroup of 4 waves per (sequence b, K/V head g, split s).
-// The group's n_rep query heads are the 16 columns of the matrix-core tiles
-// (padded with zero queries), so every cached K/V row is read from HBM once
-// and used by all heads of its group:
+// Work unit: one workgroup of 1, 2 or 4 waves per (sequence b, K/V head g,
+// split s).  The group's n_rep query heads are the 16 columns of the
+// matrix-core tiles (padded with zero queries), so every cached K/V row is read
+// from HBM once and used by all heads of its group:
 //
 //   scores  S^T[key][head] = K[key][:] . Q[head][:]     16x16x32 bf16 MFMA,
 //           A = 16 keys x 32 dims straight from HBM (16-byte loads),
@@ -19,10 +19,14 @@
 //           B = the weights, already in the right lanes after the scores
 //
 // Each wave walks its own 32-position tiles of the split (tile t goes to wave
-// t mod 4) with a one-tile register prefetch; the four waves merge (max, sum,
-// output) through LDS at the end.  Positions at or beyond the sequence length
-// are never loaded: their K rows are zero, their scores are set to -inf before
-// the softmax and their V rows are zero, so cache contents there (NaN included)
+// t mod waves) with a one-tile register prefetch; the waves merge (max, sum,
+// output) through LDS.  With several splits, each workgroup writes its
+// partial (max, sum, output) per head; the last workgroup of a (b, g) to
+// finish -- found with a counter in the workspace header, which it resets --
+// merges the partials (log-sum-exp) and writes the output, so one launch does
+// the whole step.  Positions at or beyond the sequence length are never
+// loaded: their K rows are zero, their scores are set to -inf before the
+// softmax and their V rows are zero, so cache contents there (NaN included)
 // cannot reach the arithmetic.
 
 #include "device_common.h"
@@ -32,7 +36,7 @@ namespace gqa {
 namespace {
 
 constexpr int kKT = 32;        // positions per wave step
-constexpr int kWaves = 4;
+constexpr int kMaxWaves = 4;
 
 template <int D>
 struct Cfg {
@@ -43,21 +47,117 @@ struct Cfg {
   static constexpr int kPitch = D * 2 + 16;       // LDS bytes per V row (bank spread)
   static constexpr int kWaveLds = kKT * kPitch;
   static constexpr int kMergeRow = D + 4;         // floats per head row in the merge area
-  static constexpr int kMergeBytes = (kWaves * 16 * kMergeRow + 2 * kWaves * 16) * 4;
-  static constexpr int kLds = kWaves * kWaveLds > kMergeBytes ? kWaves * kWaveLds : kMergeBytes;
+  static constexpr int kMergeBytes = (kMaxWaves * 16 * kMergeRow + 3 * kMaxWaves * 16 + 32) * 4;
+  static constexpr int kLds = kMaxWaves * kWaveLds > kMergeBytes ? kMaxWaves * kWaveLds : kMergeBytes;
 };
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Partials cross workgroups (and XCDs, whose L2s are not coherent with each
+// other).  They are written and read with buffer instructions carrying the
+// device-coherence bit (sc1) -- the same access an agent-scope relaxed atomic
+// makes, but 16 bytes wide and free to overlap -- so no device-wide cache
+// writeback or invalidate is needed.  A buffer load past the end of its
+// resource returns zeros.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kDeviceCoherent = 16;    // cache-policy bit sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Log-sum-exp merge of the S split partials of NI (head, 8-column chunk)
+// items of sequence b, written to out.  Splits are read 8 at a time with all
+// their loads (for every item) in flight together; the running maximum is
+// rescaled per batch.
+template <int D, int NI>
+__device__ __forceinline__ void merge_items(const DecodeProblem& p, int b, const int* hs, const int* c8s) {
+  const int S = p.num_splits;
+  __amdgpu_buffer_rsrc_t rml[NI], ro[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int64_t pr0 = (int64_t(b) * p.H + hs[i]) * S;
+    rml[i] = rsrc(p.part_ml + pr0 * 2, uint32_t(S) * 8u);
+    ro[i] = rsrc(p.part_o + pr0 * D, uint32_t(S) * D * 4u);
+  }
+  float M[NI], L[NI], O[NI][8];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    M[i] = -INFINITY;
+    L[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) O[i][e] = 0.f;
+  }
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    u32x2_t ml[NI][8];
+    u32x4_t oa[NI][8], ob[NI][8];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int s = s0 + u;                      // s >= S reads zeros (l = 0: skipped)
+        ml[i][u] = __builtin_amdgcn_raw_buffer_load_b64(rml[i], s * 8, 0, kDeviceCoherent);
+        oa[i][u] = __builtin_amdgcn_raw_buffer_load_b128(ro[i], s * D * 4 + c8s[i] * 32, 0, kDeviceCoherent);
+        ob[i][u] = __builtin_amdgcn_raw_buffer_load_b128(ro[i], s * D * 4 + c8s[i] * 32 + 16, 0, kDeviceCoherent);
+      }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float cm = M[i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (__uint_as_float(ml[i][u][1]) > 0.f) cm = fmaxf(cm, __uint_as_float(ml[i][u][0]));
+      if (cm == -INFINITY) continue;             // nothing seen yet
+      const float f0 = exp2f(M[i] - cm);         // 0 while M is -inf
+      L[i] *= f0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) O[i][e] *= f0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float lu = __uint_as_float(ml[i][u][1]);
+        const float f = lu > 0.f ? exp2f(__uint_as_float(ml[i][u][0]) - cm) : 0.f;
+        L[i] = fmaf(lu, f, L[i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          O[i][e] = fmaf(__uint_as_float(oa[i][u][e]), f, O[i][e]);
+          O[i][4 + e] = fmaf(__uint_as_float(ob[i][u][e]), f, O[i][4 + e]);
+        }
+      }
+      M[i] = cm;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const float inv = L[i] > 0.f ? 1.f / L[i] : 0.f;
+    u32x4_t w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(O[i][2 * e] * inv, O[i][2 * e + 1] * inv);
+    st16(p.out + (int64_t(b) * p.H + hs[i]) * D + c8s[i] * 8, w);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void merge_splits(const DecodeProblem& p, int b, int h, int c8) {
+  merge_items<D, 1>(p, b, &h, &c8);
+}
+
+template <int D>
+__device__ __forceinline__ void merge_splits2(const DecodeProblem& p, int b, int h0, int c0, int h1, int c1) {
+  const int hs[2] = {h0, h1};
+  const int cs[2] = {c0, c1};
+  merge_items<D, 2>(p, b, hs, cs);
+}
+
 template <int D, int NHB>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::kLds];
+  __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
   const int lo = lane & 15;
   const int hi = lane >> 4;
 
@@ -114,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
 #pragma unroll
       for (int ks = 0; ks < C::kSteps; ++ks) {
         u32x4_t w = {0u, 0u, 0u, 0u};
-        if (key < j1) w = ld16(kb + int64_t(key) * D + (4 * ks + hi) * 8);
+        if (key < j1) w = ld16_stream(kb + int64_t(key) * D + (4 * ks + hi) * 8);
         kreg[blk][ks] = w;
       }
     }
@@ -124,14 +224,14 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
       const int key = jt + idx / C::kChunks;
       const int ch = idx % C::kChunks;
       u32x4_t w = {0u, 0u, 0u, 0u};
-      if (key < j1) w = ld16(vb + int64_t(key) * D + ch * 8);
+      if (key < j1) w = ld16_stream(vb + int64_t(key) * D + ch * 8);
       vreg[t] = w;
     }
   };
 
   int jt = j0 + wave * kKT;
   if (jt < j1) load_tile(jt);
-  for (; jt < j1; jt += kWaves * kKT) {
+  for (; jt < j1; jt += nw * kKT) {
     u32x4_t kc[2][C::kSteps];
     u32x4_t vc[C::kVLoads];
 #pragma unroll
@@ -140,7 +240,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
       for (int ks = 0; ks < C::kSteps; ++ks) kc[blk][ks] = kreg[blk][ks];
 #pragma unroll
     for (int t = 0; t < C::kVLoads; ++t) vc[t] = vreg[t];
-    if (jt + kWaves * kKT < j1) load_tile(jt + kWaves * kKT);
+    if (jt + nw * kKT < j1) load_tile(jt + nw * kKT);
 
     // V rows of this tile into the wave's LDS area (row-major, padded rows)
 #pragma unroll
@@ -226,11 +326,16 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
     lrun[hb] = x;
   }
 
-  // merge the four waves, one head block at a time
+  // Merge the waves, one head block at a time, and write the output (one
+  // split) or this split's partial result.  One thread per head computes the
+  // merged maximum, the per-wave factors and the normaliser; then every thread
+  // combines 4 output columns of one head.
   float* sm_o = reinterpret_cast<float*>(smem);
-  float* sm_m = sm_o + kWaves * 16 * C::kMergeRow;
-  float* sm_l = sm_m + kWaves * 16;
-  constexpr int kC8 = D / 8;
+  float* sm_m = sm_o + kMaxWaves * 16 * C::kMergeRow;
+  float* sm_l = sm_m + kMaxWaves * 16;
+  float* sm_f = sm_l + kMaxWaves * 16;
+  float* sm_hd = sm_f + kMaxWaves * 16;      // per head: merged max, then normaliser (or 1/it)
+  constexpr int kC4 = D / 4;
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     __syncthreads();
@@ -242,44 +347,79 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
       sm_l[wave * 16 + lo] = lrun[hb];
     }
     __syncthreads();
-    const int nh = min(16, p.n_rep - 16 * hb);
-    for (int t = threadIdx.x; t < nh * kC8; t += 256) {
-      const int hl = t / kC8;
-      const int c8 = t % kC8;
+    if (threadIdx.x < 16) {
+      const int hl = threadIdx.x;
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-        if (sm_l[w * 16 + hl] > 0.f) M = fmaxf(M, sm_m[w * 16 + hl]);
+      for (int w = 0; w < kMaxWaves; ++w)
+        if (w < nw && sm_l[w * 16 + hl] > 0.f) M = fmaxf(M, sm_m[w * 16 + hl]);
       float L = 0.f;
-      float O[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float lw = sm_l[w * 16 + hl];
-        if (lw > 0.f) {
-          const float f = exp2f(sm_m[w * 16 + hl] - M);
+      for (int w = 0; w < kMaxWaves; ++w) {
+        if (w < nw) {
+          const float lw = sm_l[w * 16 + hl];
+          const float f = lw > 0.f ? exp2f(sm_m[w * 16 + hl] - M) : 0.f;
+          sm_f[w * 16 + hl] = f;
           L = fmaf(lw, f, L);
-          const float* src = sm_o + (w * 16 + hl) * C::kMergeRow + c8 * 8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) O[e] = fmaf(src[e], f, O[e]);
         }
       }
+      sm_hd[hl] = M;
+      sm_hd[16 + hl] = S == 1 ? (L > 0.f ? 1.f / L : 0.f) : L;
+    }
+    __syncthreads();
+    const int nh = min(16, p.n_rep - 16 * hb);
+    for (int t = threadIdx.x; t < nh * kC4; t += blockDim.x) {
+      const int hl = t / kC4;
+      const int c4 = t % kC4;
+      f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kMaxWaves; ++w)
+        if (w < nw) O += sm_f[w * 16 + hl] * *reinterpret_cast<const f32x4_t*>(sm_o + (w * 16 + hl) * C::kMergeRow + c4 * 4);
       const int h = g * p.n_rep + 16 * hb + hl;
       if (S == 1) {
-        u32x4_t w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(L > 0.f ? O[2 * e] / L : 0.f, L > 0.f ? O[2 * e + 1] / L : 0.f);
-        st16(p.out + (int64_t(b) * p.H + h) * D + c8 * 8, w);
+        const float inv = sm_hd[16 + hl];
+        *reinterpret_cast<uint2*>(p.out + (int64_t(b) * p.H + h) * D + c4 * 4) =
+            make_uint2(pack_bf16x2(O[0] * inv, O[1] * inv), pack_bf16x2(O[2] * inv, O[3] * inv));
       } else {
         const int64_t pr = (int64_t(b) * p.H + h) * S + s;
-        float* dst = p.part_o + pr * D + c8 * 8;
-        st16(dst, u32x4_t{__float_as_uint(O[0]), __float_as_uint(O[1]), __float_as_uint(O[2]), __float_as_uint(O[3])});
-        st16(dst + 4, u32x4_t{__float_as_uint(O[4]), __float_as_uint(O[5]), __float_as_uint(O[6]), __float_as_uint(O[7])});
-        if (c8 == 0) {
-          p.part_ml[pr * 2] = M;
-          p.part_ml[pr * 2 + 1] = L;
+        const __amdgpu_buffer_rsrc_t ro = rsrc(p.part_o + pr * D, D * 4u);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4_t{__float_as_uint(O[0]), __float_as_uint(O[1]), __float_as_uint(O[2]), __float_as_uint(O[3])},
+            ro, c4 * 16, 0, kDeviceCoherent);
+        if (c4 == 0) {
+          const __amdgpu_buffer_rsrc_t rml = rsrc(p.part_ml + pr * 2, 8u);
+          __builtin_amdgcn_raw_buffer_store_b64(
+              u32x2_t{__float_as_uint(sm_hd[hl]), __float_as_uint(sm_hd[16 + hl])}, rml, 0, 0, kDeviceCoherent);
         }
       }
     }
+  }
+  if (S == 1 || p.counters == nullptr) return;
+
+  // Split merge by the last workgroup of this (b, g) to finish.  Each thread
+  // waits until its device-coherent partial stores are acknowledged before the
+  // workgroup counts itself in; the workgroup that completes the count reads
+  // every partial back with device-coherent loads issued after that.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = atomicAdd(p.counters + unit, 1);
+    s_last = (old == S - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0)            // ready for the next call (nothing reads it in this one)
+    __hip_atomic_store(p.counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  constexpr int kC8 = D / 8;
+  const int items = p.n_rep * kC8;
+  const int t0 = threadIdx.x;
+  const int t1 = threadIdx.x + blockDim.x;
+  if (t1 < items) {
+    merge_splits2<D>(p, b, g * p.n_rep + t0 / kC8, t0 % kC8, g * p.n_rep + t1 / kC8, t1 % kC8);
+    for (int t = t1 + blockDim.x; t < items; t += blockDim.x)
+      merge_splits<D>(p, b, g * p.n_rep + t / kC8, t % kC8);
+  } else if (t0 < items) {
+    merge_splits<D>(p, b, g * p.n_rep + t0 / kC8, t0 % kC8);
   }
 }
 
@@ -288,7 +428,11 @@ hipError_t launch_t(const DecodeProblem& p, hipStream_t stream) {
   const int64_t blocks = int64_t(p.B) * p.G * p.num_splits;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_mfma_kernel<D, NHB>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  // one wave per 32-position tile of a split, at most four
+  const int tiles = (p.split_len + kKT - 1) / kKT;
+  const int waves = tiles >= 4 ? 4 : (tiles >= 2 ? 2 : 1);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, NHB>), dim3(unsigned(blocks)), dim3(64 * waves), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

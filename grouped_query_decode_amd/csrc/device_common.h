@@ -35,6 +35,10 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
 __device__ __forceinline__ u32x4_t ld16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
+// 16-byte load of data read once (non-temporal hint: streams past the caches).
+__device__ __forceinline__ u32x4_t ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
 __device__ __forceinline__ void st16(void* p, u32x4_t v) {
   *reinterpret_cast<u32x4_t*>(p) = v;
 }

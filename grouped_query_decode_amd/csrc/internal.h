@@ -42,6 +42,7 @@ struct DecodeProblem {
   uint16_t* out;            // [B, H, d]
   float* part_o;
   float* part_ml;
+  int* counters;            // [B*G] split-arrival counters (zero between calls), or null
   int B, H, G, n_rep, d, n_max;
   float scale;
   int num_splits, split_len;

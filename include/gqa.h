@@ -56,8 +56,10 @@ typedef enum gqa_status {
  *
  * A decode call divides each sequence's cache into num_splits slices, runs
  * one pass per slice and, when num_splits > 1, merges the slices' partial
- * softmax results (log-sum-exp) in a second pass.  The partial results live in
- * a caller-provided workspace.
+ * softmax results (log-sum-exp): inside the same launch (the last slice of a
+ * (sequence, K/V head) to finish merges), or in a second launch when there are
+ * more than 16384 (sequence, K/V head) pairs or the float32 path runs.  The
+ * partial results live in a caller-provided workspace.
  *
  * gqa_decode_num_splits() returns the split count gqa_decode() uses.  It is a
  * pure function of the shape (it reads no device and no sequence length), so
@@ -67,6 +69,14 @@ typedef enum gqa_status {
  * gqa_decode_workspace_bytes(): bytes of workspace that a decode of this
  * shape needs with num_splits slices (num_splits = 0: the planner's choice).
  * 0 means no workspace is needed.  Returns (size_t)-1 for an invalid shape.
+ *
+ * Workspace contract: a device buffer, 16-byte aligned.  Its first 64 KiB hold
+ * one arrival counter per (sequence, K/V head), which lets the last split to
+ * finish merge the others inside the same kernel launch.  The caller
+ * zero-fills the buffer ONCE before its first use (e.g. hipMemset at
+ * allocation); every completed call leaves those 64 KiB zero again, so the
+ * same buffer can then be reused for any shape without clearing.  Calls that
+ * share a workspace must not overlap in time (use one workspace per stream).
  */
 int gqa_decode_num_splits(int B, int H, int G, int d, int n_max);
 size_t gqa_decode_workspace_bytes(int B, int H, int G, int d, int n_max, int num_splits);
@@ -96,8 +106,9 @@ size_t gqa_decode_workspace_bytes(int B, int H, int G, int d, int n_max, int num
  *   d        64 or 128 (anything else: GQA_ERR_UNSUPPORTED).
  *   workspace/workspace_bytes   device buffer of at least
  *                               gqa_decode_workspace_bytes(B,H,G,d,n_max,0)
- *                               bytes; may be NULL/0 when that is 0.  Its
- *                               contents on entry do not matter.
+ *                               bytes, zero-filled before its first use (see
+ *                               the workspace contract above); may be NULL/0
+ *                               when that size is 0.
  *
  * Errors: GQA_ERR_INVALID_ARG for B, H, G, n_max < 0 or H, G < 1 with B > 0,
  * H % G != 0, a NULL or misaligned tensor, an unknown dtype or a non-finite
