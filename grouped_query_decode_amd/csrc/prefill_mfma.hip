@@ -12,16 +12,22 @@
 // 128 query rows.  Per 64-key tile and wave:
 //
 //   S^T[key][row] = K[key][:] . Q[row][:]        32x32x16 bf16 MFMA (2 x 8),
-//                   A = K tile from LDS (XOR-swizzled 16-byte chunks),
-//                   B = the wave's queries (registers, loaded once)
+//                   A = K tile from LDS, B = the wave's queries (registers)
 //   mask j > i on tiles that reach the diagonal; online softmax in base 2,
 //   float32, one query row per lane column (max/sum in-lane plus one exchange)
 //   O^T[dim][row] += V^T[dim][key] P^T[key][row] 32x32x16 MFMA (4 x 4),
-//                   A = V^T from LDS (transposed when staged),
-//                   B = the weights, rounded to bf16, already in place
+//                   A = V^T read from the row-major V tile with the gfx950
+//                   transposing LDS load, B = the bf16 weights, already in place
 //
-// Query tiles are issued heaviest (last) first so the causal triangle
-// balances across the machine.
+// K/V tiles are double-buffered in LDS (row-major, 16-byte chunks XOR-swizzled
+// per row so that the operand reads hit distinct banks): the next tile's
+// global loads are issued before the current tile's math and land in the other
+// buffer afterwards, one barrier per tile.  Softmax work per score: one FMA
+// (scale folded in), one exp2, a third of a max3, half a bf16 pack, half a
+// bf16 dot2 for the normaliser (which sums the rounded weights); the running
+// output is rescaled only when some row's maximum grew.  Query tiles are issued
+// heaviest first, and the query tiles of a (b, g) stay on one XCD (consecutive
+// workgroups go to consecutive XCDs) so its K/V stays in that XCD's L2.
 
 #include "device_common.h"
 #include "internal.h"
@@ -31,6 +37,9 @@ namespace {
 
 constexpr int kKT = 64;     // keys per tile
 constexpr int kQT = 32;     // query positions per wave
+constexpr int kXcds = 8;
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct PCfg {
@@ -38,27 +47,33 @@ struct PCfg {
   static constexpr int kColBlocks = D / 32;      // PV output blocks of 32 dims
   static constexpr int kChunks = D / 8;          // 16-byte chunks per row
   static constexpr int kLoads = kKT * kChunks / 256;   // per thread per tile (K and V each)
-  static constexpr int kKBytes = kKT * D * 2;
-  static constexpr int kVPitch = kKT * 2 + 16;   // bytes per V^T row
-  static constexpr int kVBytes = D * kVPitch;
+  static constexpr int kTileBytes = kKT * D * 2;
+  static constexpr int kRowBytes = D * 2;
 };
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Position of key kl (0..63) inside a V^T row: the 8 keys that one lane feeds
-// to one PV k-step are contiguous.  kl = 16u + 8a + 4h + b  ->  16u + 8h + 4a + b.
-__device__ __forceinline__ int vt_pos(int kl) {
-  return (kl & ~15) | ((kl & 4) << 1) | ((kl & 8) >> 1) | (kl & 3);
+// 16-byte chunk swizzles inside a tile row.
+template <int D> __device__ __forceinline__ int swz_k(int row, int ch) {
+  return ch ^ (row & (D / 8 - 1));
+}
+template <int D> __device__ __forceinline__ int swz_v(int row, int ch) {
+  return ch ^ ((row << 1) & (D / 8 - 1));
+}
+
+// gfx950 transposing LDS read: within each 16-lane group, lanes 4e..4e+3
+// address row e (4 consecutive bf16 each) of a 4 x 16 block, and lane i
+// receives column i of the 4 rows.
+__device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(const_cast<char*>(p)));
 }
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) {
   using C = PCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[C::kKBytes + C::kVBytes];
-  char* sk = smem;
-  char* sv = smem + C::kKBytes;
+  __shared__ __attribute__((aligned(16))) char smem[4 * C::kTileBytes];   // K0 V0 K1 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -72,8 +87,19 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) 
   const int rows_wg = kQT * tb_per_wg;
   const int n_qt = (p.T + rows_wg - 1) / rows_wg;
   const int units = p.B * p.G * n_hq;
-  const int qt = n_qt - 1 - int(blockIdx.x / unsigned(units));
-  const int unit = int(blockIdx.x % unsigned(units));
+  int unit, qt_rank;
+  if (units % kXcds == 0) {
+    // keep a unit's query tiles on one XCD: workgroup i runs on XCD i % 8
+    const int x = int(blockIdx.x % kXcds);
+    const int i = int(blockIdx.x / kXcds);
+    const int per_xcd = units / kXcds;
+    unit = x * per_xcd + i % per_xcd;
+    qt_rank = i / per_xcd;
+  } else {
+    unit = int(blockIdx.x % unsigned(units));
+    qt_rank = int(blockIdx.x / unsigned(units));
+  }
+  const int qt = n_qt - 1 - qt_rank;              // heaviest first
   const int hq = unit % n_hq;
   const int g = (unit / n_hq) % p.G;
   const int b = unit / (n_hq * p.G);
@@ -84,7 +110,12 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) 
   const int t_last = min(p.T, (qt + 1) * rows_wg) - 1;
   const int n_kt = t_last / kKT + 1;
 
-  // queries: B operand, lane column = row l32, k-slot group h2 -> dims 16*ks + 8*h2 .. +7
+  // queries: B operand, lane column = row l32, k-slot group h2 -> dims 16*ks + 8*h2 .. +7.
+  // A negative scale is folded into the queries (exact sign flip).
+  const uint32_t qsign = p.scale < 0.f ? 0x80008000u : 0u;
+  // (a zero scale is replaced by a tiny one: the weights are then exactly
+  // uniform, and masked scores still map to exactly zero weight)
+  const float c2 = p.scale == 0.f ? 1e-30f : fabsf(p.scale) * kLog2e;
   bf16x8_t qop[C::kSteps];
   {
     const bool rv = t_row < p.T;
@@ -93,6 +124,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) 
     for (int ks = 0; ks < C::kSteps; ++ks) {
       u32x4_t w = {0u, 0u, 0u, 0u};
       if (rv) w = ld16(qrow + 16 * ks + 8 * h2);
+      w ^= u32x4_t{qsign, qsign, qsign, qsign};
       qop[ks] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
@@ -102,9 +134,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) 
   for (int cb = 0; cb < C::kColBlocks; ++cb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
-  float mrun = -INFINITY;
-  float lrun = 0.f;
-  const float c2 = p.scale * kLog2e;
+  float mrun = -INFINITY;     // running max of the raw scores of this lane's row
+  float lrun = 0.f;           // this lane's share of the normaliser
 
   const int64_t kv_row = int64_t(p.G) * D;           // elements between positions
   const uint16_t* kbase = p.k + (int64_t(b) * p.T * p.G + g) * D;
@@ -127,95 +158,116 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) 
       vreg[i] = wv;
     }
   };
-
-  load_tile(0);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    __syncthreads();   // previous tile's LDS reads are done
+  auto store_tile = [&](int buf) {
+    char* sk = smem + buf * 2 * C::kTileBytes;
+    char* sv = sk + C::kTileBytes;
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
       const int item = i * 256 + tid;
       const int kl = item / C::kChunks;
       const int ch = item % C::kChunks;
-      const int phys = ch ^ (kl & (C::kChunks - 1));
-      *reinterpret_cast<u32x4_t*>(sk + kl * (D * 2) + phys * 16) = kreg[i];
-      const int pos = vt_pos(kl);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t w = vreg[i][e];
-        *reinterpret_cast<uint16_t*>(sv + (ch * 8 + 2 * e) * C::kVPitch + pos * 2) = uint16_t(w & 0xffffu);
-        *reinterpret_cast<uint16_t*>(sv + (ch * 8 + 2 * e + 1) * C::kVPitch + pos * 2) = uint16_t(w >> 16);
-      }
+      *reinterpret_cast<u32x4_t*>(sk + kl * C::kRowBytes + swz_k<D>(kl, ch) * 16) = kreg[i];
+      *reinterpret_cast<u32x4_t*>(sv + kl * C::kRowBytes + swz_v<D>(kl, ch) * 16) = vreg[i];
     }
-    __syncthreads();
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
     if (kt + 1 < n_kt) load_tile(kt + 1);
+    const char* sk = smem + buf * 2 * C::kTileBytes;
+    const char* sv = sk + C::kTileBytes;
 
     const int key0 = kt * kKT;
-    if (key0 > t_base + kQT - 1) continue;        // tile entirely after this wave's rows
-    const bool diag = key0 + kKT - 1 > t_base;     // some key may follow some row
+    if (key0 <= t_base + kQT - 1) {                 // some key precedes some row of this wave
+      const bool diag = key0 + kKT - 1 > t_base;    // some key may follow some row
 
-    // scores: lane holds S^T[key0 + 32*kb + 8*(r/4) + 4*h2 + r%4][t_row]
-    f32x16_t sacc[2];
+      // scores: lane holds S^T[key0 + 32*kb + 8*(r/4) + 4*h2 + r%4][t_row]
+      f32x16_t sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16_t a;
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16_t a;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) a[r] = 0.f;
-      const int kl = 32 * kb + l32;
+        for (int r = 0; r < 16; ++r) a[r] = 0.f;
+        const int kl = 32 * kb + l32;
 #pragma unroll
-      for (int ks = 0; ks < C::kSteps; ++ks) {
-        const int phys = (2 * ks + h2) ^ (kl & (C::kChunks - 1));
-        const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(sk + kl * (D * 2) + phys * 16);
-        a = mfma32(__builtin_bit_cast(bf16x8_t, kw), qop[ks], a);
-      }
-      sacc[kb] = a;
-    }
-
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sacc[kb][r] * c2;
-        if (diag) {
-          const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          x = (key > t_row || key >= p.T) ? -INFINITY : x;
+        for (int ks = 0; ks < C::kSteps; ++ks) {
+          const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(sk + kl * C::kRowBytes +
+                                                               swz_k<D>(kl, 2 * ks + h2) * 16);
+          a = mfma32(__builtin_bit_cast(bf16x8_t, kw), qop[ks], a);
         }
-        sacc[kb][r] = x;
-        tmax = fmaxf(tmax, x);
+        sacc[kb] = a;
       }
-    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    const float mn = fmaxf(mrun, tmax);            // finite: key 0 precedes every row
-    const float alpha = exp2f(mrun - mn);
-    mrun = mn;
 
-    // weights -> bf16 B operands, one per 16-key step u: keys 16u + 8*(e/4) + 4*h2 + e%4
-    bf16x8_t pop[4];
-    float lsum = 0.f;
+      if (diag) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      uint32_t w[4];
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const int r0 = 8 * (u & 1) + 2 * e2;
-        const uint32_t pk = pack_bf16x2(exp2f(sacc[u >> 1][r0] - mn), exp2f(sacc[u >> 1][r0 + 1] - mn));
-        w[e2] = pk;
-        lsum += bf16lo_to_f32(pk) + bf16hi_to_f32(pk);
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            if (key > t_row || key >= p.T) sacc[kb][r] = -INFINITY;
+          }
       }
-      pop[u] = __builtin_bit_cast(bf16x8_t, u32x4_t{w[0], w[1], w[2], w[3]});
-    }
-    lrun = fmaf(lrun, alpha, lsum);
+      float tmax = mrun;
 #pragma unroll
-    for (int cb = 0; cb < C::kColBlocks; ++cb) acc[cb] *= alpha;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) tmax = fmaxf(fmaxf(tmax, sacc[kb][r]), sacc[kb][r + 1]);
+      const float mn = fmaxf(tmax, shfl_xor(tmax, 32));   // finite: key 0 precedes every row
+      const float mc = mn * c2;
+      if (__any(mn != mrun)) {                     // some row's maximum grew: rescale
+        const float alpha = mrun == -INFINITY ? 0.f : exp2f(mrun * c2 - mc);
+        lrun *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < C::kColBlocks; ++cb) acc[cb] *= alpha;
+        mrun = mn;
+      }
 
+      // weights -> bf16 B operands, one per 16-key step u: keys 16u + 8*(e/4) + 4*h2 + e%4
+      bf16x8_t pop[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 4; ++u) {
+        uint32_t w[4];
 #pragma unroll
-      for (int cb = 0; cb < C::kColBlocks; ++cb) {
-        const int row = 32 * cb + l32;
-        const u32x4_t vw = *reinterpret_cast<const u32x4_t*>(sv + row * C::kVPitch + (16 * u + 8 * h2) * 2);
-        acc[cb] = mfma32(__builtin_bit_cast(bf16x8_t, vw), pop[u], acc[cb]);
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int r0 = 8 * (u & 1) + 2 * e2;
+          const float p0 = exp2f(fmaf(sacc[u >> 1][r0], c2, -mc));
+          const float p1 = exp2f(fmaf(sacc[u >> 1][r0 + 1], c2, -mc));
+          w[e2] = pack_bf16x2(p0, p1);
+          lrun = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e2]),
+                                                 __builtin_bit_cast(bf16x2_t, 0x3f803f80u), lrun, false);
+        }
+        pop[u] = __builtin_bit_cast(bf16x8_t, u32x4_t{w[0], w[1], w[2], w[3]});
+      }
+
+      // O^T += V^T P^T; V^T operand via transposing reads of the row-major V tile:
+      // lane (16-lane group grp, index i) gets column 32*cb + 16*(grp%2) + i of
+      // keys 16u + 4*h2 + 0..3 (first read) and 16u + 8 + 4*h2 + 0..3 (second).
+      const int grp = lane >> 4;
+      const int li = lane & 15;
+      const int e_row = li >> 2;
+      const int m4 = li & 3;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row0 = 16 * u + 4 * h2 + e_row;
+        const int row1 = row0 + 8;
+#pragma unroll
+        for (int cb = 0; cb < C::kColBlocks; ++cb) {
+          const int ch = 4 * cb + 2 * (grp & 1) + (m4 >> 1);
+          const int boff = 8 * (m4 & 1);
+          const i16x4_t lo4 = lds_read_tr16(sv + row0 * C::kRowBytes + swz_v<D>(row0, ch) * 16 + boff);
+          const i16x4_t hi4 = lds_read_tr16(sv + row1 * C::kRowBytes + swz_v<D>(row1, ch) * 16 + boff);
+          const bf16x8_t vop = __builtin_bit_cast(
+              bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[cb] = mfma32(vop, pop[u], acc[cb]);
+        }
       }
     }
+
+    if (kt + 1 < n_kt) store_tile(buf ^ 1);
+    __syncthreads();
   }
 
   const float l = lrun + shfl_xor(lrun, 32);
