@@ -12,7 +12,7 @@
 //   scores  S^T[key][head] = K[key][:] . Q[head][:]     16x16x32 bf16 MFMA,
 //           A = 16 keys x 32 dims straight from HBM (16-byte loads),
 //           B = the group's queries (registers, loaded once)
-//   softmax online, base 2, float32; the weights are rounded to bf16 and the
+//   softmax online, base 2 (hardware exp2), float32; the weights are rounded to bf16 and the
 //           normaliser sums the rounded weights (so constant V is exact)
 //   output  O^T[dim][head] += V^T[dim][key] P^T[key][head]   16x16x32 MFMA,
 //           A = V^T gathered from a per-wave LDS copy of the 32-row V tile,
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
       tmax = fmaxf(tmax, shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, shfl_xor(tmax, 32));
       const float mn = fmaxf(mrun[hb], tmax);      // finite: position jt is valid
-      const float alpha = exp2f(mrun[hb] - mn);
+      const float alpha = __builtin_amdgcn_exp2f(mrun[hb] - mn);
       mrun[hb] = mn;
       uint32_t w[4];
       float lsum = 0.f;
@@ -290,7 +290,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r2 = 0; r2 < 2; ++r2) {
-          const uint32_t pk = pack_bf16x2(exp2f(t2[blk][2 * r2] - mn), exp2f(t2[blk][2 * r2 + 1] - mn));
+          const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(t2[blk][2 * r2] - mn),
+                                          __builtin_amdgcn_exp2f(t2[blk][2 * r2 + 1] - mn));
           w[blk * 2 + r2] = pk;
           lsum += bf16lo_to_f32(pk) + bf16hi_to_f32(pk);
         }

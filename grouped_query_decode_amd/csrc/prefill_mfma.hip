@@ -19,11 +19,12 @@
 //                   A = V^T read from the row-major V tile with the gfx950
 //                   transposing LDS load, B = the bf16 weights, already in place
 //
-// K/V tiles are double-buffered in LDS (row-major, 16-byte chunks XOR-swizzled
-// per row so that the operand reads hit distinct banks): the next tile's
+// K/V tiles are double-buffered in LDS (row-major, rows padded so that the
+// operand reads hit distinct banks): the next tile's
 // global loads are issued before the current tile's math and land in the other
 // buffer afterwards, one barrier per tile.  Softmax work per score: one FMA
-// (scale folded in), one exp2, a third of a max3, half a bf16 pack, half a
+// (scale folded in), one hardware exp2 (weights below 2^-126 may flush to
+// zero), a third of a max3, half a bf16 pack, half a
 // bf16 dot2 for the normaliser (which sums the rounded weights); the running
 // output is rescaled only when some row's maximum grew.  Query tiles are issued
 // heaviest first, and the query tiles of a (b, g) stay on one XCD (consecutive
@@ -41,26 +42,27 @@ constexpr int kXcds = 8;
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
+// LDS tile rows are padded so that the operand reads hit distinct banks
+// (64 banks of 4 bytes): a K row is 16 bytes longer than its data (16
+// consecutive rows read at one column cover all banks with 16-byte reads), a
+// V row 32 bytes longer (the transposing reads of 4 rows x 2 chunks by a
+// 16-lane group cover 32 distinct banks).  Every operand address is then a
+// per-lane base plus a compile-time offset.
 template <int D>
 struct PCfg {
   static constexpr int kSteps = D / 16;          // QK k-steps (k = 16)
   static constexpr int kColBlocks = D / 32;      // PV output blocks of 32 dims
   static constexpr int kChunks = D / 8;          // 16-byte chunks per row
   static constexpr int kLoads = kKT * kChunks / 256;   // per thread per tile (K and V each)
-  static constexpr int kTileBytes = kKT * D * 2;
-  static constexpr int kRowBytes = D * 2;
+  static constexpr int kKPitch = D * 2 + 16;
+  static constexpr int kVPitch = D * 2 + 32;
+  static constexpr int kKBytes = kKT * kKPitch;
+  static constexpr int kVBytes = kKT * kVPitch;
+  static constexpr int kBufBytes = kKBytes + kVBytes;
 };
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// 16-byte chunk swizzles inside a tile row.
-template <int D> __device__ __forceinline__ int swz_k(int row, int ch) {
-  return ch ^ (row & (D / 8 - 1));
-}
-template <int D> __device__ __forceinline__ int swz_v(int row, int ch) {
-  return ch ^ ((row << 1) & (D / 8 - 1));
 }
 
 // gfx950 transposing LDS read: within each 16-lane group, lanes 4e..4e+3
@@ -73,7 +75,7 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) {
   using C = PCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[4 * C::kTileBytes];   // K0 V0 K1 V1
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::kBufBytes];   // K0 V0 K1 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -142,32 +144,40 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) 
   const uint16_t* vbase = p.v + (int64_t(b) * p.T * p.G + g) * D;
 
   u32x4_t kreg[C::kLoads], vreg[C::kLoads];
+  // thread's first (position, chunk) of a tile; the others are 256/kChunks positions apart
+  const int kl0 = tid / C::kChunks;
+  const int ch0 = tid % C::kChunks;
+  constexpr int kRowStep = 256 / C::kChunks;
   auto load_tile = [&](int kt) {
+    const int key0 = kt * kKT + kl0;
+    const uint16_t* kp = kbase + int64_t(key0) * kv_row + ch0 * 8;
+    const uint16_t* vp = vbase + int64_t(key0) * kv_row + ch0 * 8;
+    if (kt * kKT + kKT <= p.T) {                   // whole tile inside the prompt
 #pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int item = i * 256 + tid;
-      const int kl = item / C::kChunks;
-      const int ch = item % C::kChunks;
-      const int key = kt * kKT + kl;
-      u32x4_t wk = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
-      if (key < p.T) {
-        wk = ld16(kbase + int64_t(key) * kv_row + ch * 8);
-        wv = ld16(vbase + int64_t(key) * kv_row + ch * 8);
+      for (int i = 0; i < C::kLoads; ++i) {
+        kreg[i] = ld16(kp + int64_t(i * kRowStep) * kv_row);
+        vreg[i] = ld16(vp + int64_t(i * kRowStep) * kv_row);
       }
-      kreg[i] = wk;
-      vreg[i] = wv;
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::kLoads; ++i) {
+        u32x4_t wk = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
+        if (key0 + i * kRowStep < p.T) {
+          wk = ld16(kp + int64_t(i * kRowStep) * kv_row);
+          wv = ld16(vp + int64_t(i * kRowStep) * kv_row);
+        }
+        kreg[i] = wk;
+        vreg[i] = wv;
+      }
     }
   };
   auto store_tile = [&](int buf) {
-    char* sk = smem + buf * 2 * C::kTileBytes;
-    char* sv = sk + C::kTileBytes;
+    char* sk = smem + buf * C::kBufBytes;
+    char* sv = sk + C::kKBytes;
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) {
-      const int item = i * 256 + tid;
-      const int kl = item / C::kChunks;
-      const int ch = item % C::kChunks;
-      *reinterpret_cast<u32x4_t*>(sk + kl * C::kRowBytes + swz_k<D>(kl, ch) * 16) = kreg[i];
-      *reinterpret_cast<u32x4_t*>(sv + kl * C::kRowBytes + swz_v<D>(kl, ch) * 16) = vreg[i];
+      *reinterpret_cast<u32x4_t*>(sk + (kl0 + i * kRowStep) * C::kKPitch + ch0 * 16) = kreg[i];
+      *reinterpret_cast<u32x4_t*>(sv + (kl0 + i * kRowStep) * C::kVPitch + ch0 * 16) = vreg[i];
     }
   };
 
@@ -177,8 +187,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < n_kt) load_tile(kt + 1);
-    const char* sk = smem + buf * 2 * C::kTileBytes;
-    const char* sv = sk + C::kTileBytes;
+    const char* sk = smem + buf * C::kBufBytes;
+    const char* sv = sk + C::kKBytes;
 
     const int key0 = kt * kKT;
     if (key0 <= t_base + kQT - 1) {                 // some key precedes some row of this wave
@@ -191,11 +201,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) 
         f32x16_t a;
 #pragma unroll
         for (int r = 0; r < 16; ++r) a[r] = 0.f;
-        const int kl = 32 * kb + l32;
+        const char* krow = sk + (32 * kb + l32) * C::kKPitch + h2 * 16;
 #pragma unroll
         for (int ks = 0; ks < C::kSteps; ++ks) {
-          const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(sk + kl * C::kRowBytes +
-                                                               swz_k<D>(kl, 2 * ks + h2) * 16);
+          const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(krow + ks * 32);
           a = mfma32(__builtin_bit_cast(bf16x8_t, kw), qop[ks], a);
         }
         sacc[kb] = a;
@@ -218,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) 
       const float mn = fmaxf(tmax, shfl_xor(tmax, 32));   // finite: key 0 precedes every row
       const float mc = mn * c2;
       if (__any(mn != mrun)) {                     // some row's maximum grew: rescale
-        const float alpha = mrun == -INFINITY ? 0.f : exp2f(mrun * c2 - mc);
+        const float alpha = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun * c2 - mc);
         lrun *= alpha;
 #pragma unroll
         for (int cb = 0; cb < C::kColBlocks; ++cb) acc[cb] *= alpha;
@@ -233,8 +242,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) 
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const int r0 = 8 * (u & 1) + 2 * e2;
-          const float p0 = exp2f(fmaf(sacc[u >> 1][r0], c2, -mc));
-          const float p1 = exp2f(fmaf(sacc[u >> 1][r0 + 1], c2, -mc));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[u >> 1][r0], c2, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[u >> 1][r0 + 1], c2, -mc));
           w[e2] = pack_bf16x2(p0, p1);
           lrun = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e2]),
                                                  __builtin_bit_cast(bf16x2_t, 0x3f803f80u), lrun, false);
@@ -247,18 +256,15 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) 
       // keys 16u + 4*h2 + 0..3 (first read) and 16u + 8 + 4*h2 + 0..3 (second).
       const int grp = lane >> 4;
       const int li = lane & 15;
-      const int e_row = li >> 2;
-      const int m4 = li & 3;
+      // lane's address inside the 4 x 16 block it helps read: row li/4, columns 4*(li%4)..+3
+      const char* vlane = sv + (4 * h2 + (li >> 2)) * C::kVPitch + (16 * (grp & 1) + 4 * (li & 3)) * 2;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int row0 = 16 * u + 4 * h2 + e_row;
-        const int row1 = row0 + 8;
 #pragma unroll
         for (int cb = 0; cb < C::kColBlocks; ++cb) {
-          const int ch = 4 * cb + 2 * (grp & 1) + (m4 >> 1);
-          const int boff = 8 * (m4 & 1);
-          const i16x4_t lo4 = lds_read_tr16(sv + row0 * C::kRowBytes + swz_v<D>(row0, ch) * 16 + boff);
-          const i16x4_t hi4 = lds_read_tr16(sv + row1 * C::kRowBytes + swz_v<D>(row1, ch) * 16 + boff);
+          const char* a0 = vlane + (16 * u) * C::kVPitch + 64 * cb;
+          const i16x4_t lo4 = lds_read_tr16(a0);
+          const i16x4_t hi4 = lds_read_tr16(a0 + 8 * C::kVPitch);
           const bf16x8_t vop = __builtin_bit_cast(
               bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[cb] = mfma32(vop, pop[u], acc[cb]);
