@@ -16,8 +16,8 @@
 //   mask j > i on tiles that reach the diagonal; online softmax in base 2,
 //   float32, one query row per lane column (max/sum in-lane plus one exchange)
 //   O^T[dim][row] += V^T[dim][key] P^T[key][row] 32x32x16 MFMA (4 x 4),
-//                   A = V^T read from the row-major V tile with the gfx950
-//                   transposing LDS load, B = the bf16 weights, already in place
+//                   A = V^T from LDS (transposed once per workgroup when the
+//                   tile is staged), B = the bf16 weights, already in place
 //
 // K/V tiles are double-buffered in LDS (row-major, rows padded so that the
 // operand reads hit distinct banks): the next tile's
@@ -42,22 +42,24 @@ constexpr int kXcds = 8;
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
-// LDS tile rows are padded so that the operand reads hit distinct banks
-// (64 banks of 4 bytes): a K row is 16 bytes longer than its data (16
-// consecutive rows read at one column cover all banks with 16-byte reads), a
-// V row 32 bytes longer (the transposing reads of 4 rows x 2 chunks by a
-// 16-lane group cover 32 distinct banks).  Every operand address is then a
-// per-lane base plus a compile-time offset.
+// LDS tiles (64 banks of 4 bytes):
+//  * K row-major, rows padded by 16 bytes: 16 consecutive rows read at one
+//    column with 16-byte reads cover all banks.
+//  * V stored transposed, V^T[dim][key], rows of 64 keys padded by 16 bytes,
+//    keys permuted inside a row (vt_pos) so that the 8 keys one lane feeds to
+//    one PV k-step are contiguous: the PV operand is one 16-byte read, 16
+//    consecutive dims of a read cover all banks, and the transposing 4-byte
+//    writes of a wave (two dim rows, 64 keys) cover all banks too.
+// Every operand address is a per-lane base plus a compile-time offset.
 template <int D>
 struct PCfg {
   static constexpr int kSteps = D / 16;          // QK k-steps (k = 16)
   static constexpr int kColBlocks = D / 32;      // PV output blocks of 32 dims
   static constexpr int kChunks = D / 8;          // 16-byte chunks per row
-  static constexpr int kLoads = kKT * kChunks / 256;   // per thread per tile (K and V each)
   static constexpr int kKPitch = D * 2 + 16;
-  static constexpr int kVPitch = D * 2 + 32;
+  static constexpr int kVtPitch = kKT * 2 + 16;
   static constexpr int kKBytes = kKT * kKPitch;
-  static constexpr int kVBytes = kKT * kVPitch;
+  static constexpr int kVBytes = D * kVtPitch;
   static constexpr int kBufBytes = kKBytes + kVBytes;
 };
 
@@ -65,17 +67,19 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// gfx950 transposing LDS read: within each 16-lane group, lanes 4e..4e+3
-// address row e (4 consecutive bf16 each) of a 4 x 16 block, and lane i
-// receives column i of the 4 rows.
-__device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(const_cast<char*>(p)));
+// Position of key kl (0..63) inside a V^T row: kl = 16u + 8a + 4h + b is
+// stored at 16u + 8h + 4a + b, so that the keys one lane (k-slot half h) feeds
+// to PV k-step u -- 16u + 8*(e/4) + 4h + e%4, e = 0..7 -- are contiguous.
+__device__ __forceinline__ int vt_pos(int kl) {
+  return (kl & ~15) | ((kl & 4) << 1) | ((kl & 8) >> 1) | (kl & 3);
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) {
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillProblem p) {
   using C = PCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kBufBytes];   // K0 V0 K1 V1
+  constexpr int kThreads = 64 * NW;
+  constexpr int kLoads = kKT * C::kChunks / kThreads;     // per thread per tile (K and V each)
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::kBufBytes];   // K0 K1 V0 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) 
   const int h2 = lane >> 5;
 
   const int nre = p.n_rep < 4 ? p.n_rep : 4;      // heads per workgroup
-  const int tb_per_wg = 4 / nre;                   // 32-position blocks per workgroup
+  const int tb_per_wg = NW / nre;                  // 32-position blocks per workgroup
   const int n_hq = p.n_rep / nre;
   const int rows_wg = kQT * tb_per_wg;
   const int n_qt = (p.T + rows_wg - 1) / rows_wg;
@@ -143,138 +147,221 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillProblem p) 
   const uint16_t* kbase = p.k + (int64_t(b) * p.T * p.G + g) * D;
   const uint16_t* vbase = p.v + (int64_t(b) * p.T * p.G + g) * D;
 
-  u32x4_t kreg[C::kLoads], vreg[C::kLoads];
-  // thread's first (position, chunk) of a tile; the others are 256/kChunks positions apart
+  u32x4_t kreg[kLoads];
+  // thread's first (position, chunk) of a tile; the others are kRowStep positions apart
   const int kl0 = tid / C::kChunks;
   const int ch0 = tid % C::kChunks;
-  constexpr int kRowStep = 256 / C::kChunks;
-  auto load_tile = [&](int kt) {
+  constexpr int kRowStep = kThreads / C::kChunks;
+  auto load_rows = [&](const uint16_t* base, int kt, u32x4_t* reg) {
     const int key0 = kt * kKT + kl0;
-    const uint16_t* kp = kbase + int64_t(key0) * kv_row + ch0 * 8;
-    const uint16_t* vp = vbase + int64_t(key0) * kv_row + ch0 * 8;
+    const uint16_t* ptr = base + int64_t(key0) * kv_row + ch0 * 8;
     if (kt * kKT + kKT <= p.T) {                   // whole tile inside the prompt
 #pragma unroll
-      for (int i = 0; i < C::kLoads; ++i) {
-        kreg[i] = ld16(kp + int64_t(i * kRowStep) * kv_row);
-        vreg[i] = ld16(vp + int64_t(i * kRowStep) * kv_row);
-      }
+      for (int i = 0; i < kLoads; ++i) reg[i] = ld16(ptr + int64_t(i * kRowStep) * kv_row);
     } else {
 #pragma unroll
-      for (int i = 0; i < C::kLoads; ++i) {
-        u32x4_t wk = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
-        if (key0 + i * kRowStep < p.T) {
-          wk = ld16(kp + int64_t(i * kRowStep) * kv_row);
-          wv = ld16(vp + int64_t(i * kRowStep) * kv_row);
-        }
-        kreg[i] = wk;
-        vreg[i] = wv;
+      for (int i = 0; i < kLoads; ++i) {
+        u32x4_t w = {0u, 0u, 0u, 0u};
+        if (key0 + i * kRowStep < p.T) w = ld16(ptr + int64_t(i * kRowStep) * kv_row);
+        reg[i] = w;
       }
     }
   };
-  auto store_tile = [&](int buf) {
-    char* sk = smem + buf * C::kBufBytes;
-    char* sv = sk + C::kKBytes;
+  // V tiles: each thread loads key pairs (2p, 2p+1) x one 16-byte chunk; a
+  // wave's lanes cover 32 pairs x 2 chunks (so that its transposed writes
+  // below hit all banks)
+  constexpr int kVPairItems = 32 * C::kChunks;
+  constexpr int kVItems = (kVPairItems + kThreads - 1) / kThreads;
+  u32x4_t vpr[kVItems][2];
+  auto load_vpairs = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      *reinterpret_cast<u32x4_t*>(sk + (kl0 + i * kRowStep) * C::kKPitch + ch0 * 16) = kreg[i];
-      *reinterpret_cast<u32x4_t*>(sv + (kl0 + i * kRowStep) * C::kVPitch + ch0 * 16) = vreg[i];
+    for (int j = 0; j < kVItems; ++j) {
+      const int item = tid + j * kThreads;
+      const int pr = item & 31;
+      const int ch = 2 * (item >> 6) + ((item >> 5) & 1);
+      const int key = kt * kKT + 2 * pr;
+      u32x4_t w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+      if (item < kVPairItems) {
+        const uint16_t* ptr = vbase + int64_t(key) * kv_row + ch * 8;
+        if (key < p.T) w0 = ld16(ptr);
+        if (key + 1 < p.T) w1 = ld16(ptr + kv_row);
+      }
+      vpr[j][0] = w0;
+      vpr[j][1] = w1;
+    }
+  };
+  auto store_vt = [&](char* dst) {
+#pragma unroll
+    for (int j = 0; j < kVItems; ++j) {
+      const int item = tid + j * kThreads;
+      if (item < kVPairItems) {
+        const int pr = item & 31;
+        const int ch = 2 * (item >> 6) + ((item >> 5) & 1);
+        char* col = dst + (8 * ch) * C::kVtPitch + vt_pos(2 * pr) * 2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // (V[2p][8ch + 2e], V[2p+1][8ch + 2e]) and the odd dims
+          *reinterpret_cast<uint32_t*>(col + (2 * e) * C::kVtPitch) =
+              __builtin_amdgcn_perm(vpr[j][1][e], vpr[j][0][e], 0x05040100u);
+          *reinterpret_cast<uint32_t*>(col + (2 * e + 1) * C::kVtPitch) =
+              __builtin_amdgcn_perm(vpr[j][1][e], vpr[j][0][e], 0x07060302u);
+        }
+      }
+    }
+  };
+  // LDS: K slots 0, 1 then V^T slots 0, 1 (see PCfg)
+  auto kslot = [&](int s) { return smem + s * C::kKBytes; };
+  auto vslot = [&](int s) { return smem + 2 * C::kKBytes + s * C::kVBytes; };
+  auto store_rows = [&](char* dst, int pitch, const u32x4_t* reg) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+      *reinterpret_cast<u32x4_t*>(dst + (kl0 + i * kRowStep) * pitch + ch0 * 16) = reg[i];
+  };
+
+  // scores of one tile: lane holds S^T[key0 + 32*kb + 8*(r/4) + 4*h2 + r%4][t_row];
+  // two independent accumulator chains (key blocks kb = 0, 1) interleaved
+  auto qk = [&](const char* sk, f32x16_t* sc) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+    const char* krow0 = sk + l32 * C::kKPitch + h2 * 16;
+#pragma unroll
+    for (int ks = 0; ks < C::kSteps; ++ks) {
+      const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(krow0 + ks * 32);
+      const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(krow0 + 32 * C::kKPitch + ks * 32);
+      sc[0] = mfma32(__builtin_bit_cast(bf16x8_t, k0), qop[ks], sc[0]);
+      sc[1] = mfma32(__builtin_bit_cast(bf16x8_t, k1), qop[ks], sc[1]);
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
-    const char* sk = smem + buf * C::kBufBytes;
-    const char* sv = sk + C::kKBytes;
-
-    const int key0 = kt * kKT;
-    if (key0 <= t_base + kQT - 1) {                 // some key precedes some row of this wave
-      const bool diag = key0 + kKT - 1 > t_base;    // some key may follow some row
-
-      // scores: lane holds S^T[key0 + 32*kb + 8*(r/4) + 4*h2 + r%4][t_row]
-      f32x16_t sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16_t a;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) a[r] = 0.f;
-        const char* krow = sk + (32 * kb + l32) * C::kKPitch + h2 * 16;
-#pragma unroll
-        for (int ks = 0; ks < C::kSteps; ++ks) {
-          const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(krow + ks * 32);
-          a = mfma32(__builtin_bit_cast(bf16x8_t, kw), qop[ks], a);
-        }
-        sacc[kb] = a;
-      }
-
-      if (diag) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            if (key > t_row || key >= p.T) sacc[kb][r] = -INFINITY;
-          }
-      }
-      float tmax = mrun;
+  // Online softmax of one tile's scores (masked near the diagonal): bf16
+  // weights as PV B operands (one per 16-key step u: keys 16u + 8*(e/4) +
+  // 4*h2 + e%4), the new running maximum, and the factor the running output
+  // must be scaled by before these weights are added to it.
+  auto softmax = [&](f32x16_t* sc, int key0, bool masked, bf16x8_t* pop, float& alpha, bool& rescale) {
+    if (masked) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) tmax = fmaxf(fmaxf(tmax, sacc[kb][r]), sacc[kb][r + 1]);
-      const float mn = fmaxf(tmax, shfl_xor(tmax, 32));   // finite: key 0 precedes every row
-      const float mc = mn * c2;
-      if (__any(mn != mrun)) {                     // some row's maximum grew: rescale
-        const float alpha = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun * c2 - mc);
-        lrun *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < C::kColBlocks; ++cb) acc[cb] *= alpha;
-        mrun = mn;
-      }
-
-      // weights -> bf16 B operands, one per 16-key step u: keys 16u + 8*(e/4) + 4*h2 + e%4
-      bf16x8_t pop[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int r0 = 8 * (u & 1) + 2 * e2;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[u >> 1][r0], c2, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[u >> 1][r0 + 1], c2, -mc));
-          w[e2] = pack_bf16x2(p0, p1);
-          lrun = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e2]),
-                                                 __builtin_bit_cast(bf16x2_t, 0x3f803f80u), lrun, false);
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          if (key > t_row || key >= p.T) sc[kb][r] = -INFINITY;
         }
-        pop[u] = __builtin_bit_cast(bf16x8_t, u32x4_t{w[0], w[1], w[2], w[3]});
-      }
-
-      // O^T += V^T P^T; V^T operand via transposing reads of the row-major V tile:
-      // lane (16-lane group grp, index i) gets column 32*cb + 16*(grp%2) + i of
-      // keys 16u + 4*h2 + 0..3 (first read) and 16u + 8 + 4*h2 + 0..3 (second).
-      const int grp = lane >> 4;
-      const int li = lane & 15;
-      // lane's address inside the 4 x 16 block it helps read: row li/4, columns 4*(li%4)..+3
-      const char* vlane = sv + (4 * h2 + (li >> 2)) * C::kVPitch + (16 * (grp & 1) + 4 * (li & 3)) * 2;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int cb = 0; cb < C::kColBlocks; ++cb) {
-          const char* a0 = vlane + (16 * u) * C::kVPitch + 64 * cb;
-          const i16x4_t lo4 = lds_read_tr16(a0);
-          const i16x4_t hi4 = lds_read_tr16(a0 + 8 * C::kVPitch);
-          const bf16x8_t vop = __builtin_bit_cast(
-              bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[cb] = mfma32(vop, pop[u], acc[cb]);
-        }
-      }
     }
+    float tmax = mrun;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) tmax = fmaxf(fmaxf(tmax, sc[kb][r]), sc[kb][r + 1]);
+    const float mn = fmaxf(tmax, shfl_xor(tmax, 32));   // finite: key 0 precedes every row
+    const float mc = mn * c2;
+    float lsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int r0 = 8 * (u & 1) + 2 * e2;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[u >> 1][r0], c2, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[u >> 1][r0 + 1], c2, -mc));
+        w[e2] = pack_bf16x2(p0, p1);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e2]),
+                                               __builtin_bit_cast(bf16x2_t, 0x3f803f80u), lsum, false);
+      }
+      pop[u] = __builtin_bit_cast(bf16x8_t, u32x4_t{w[0], w[1], w[2], w[3]});
+    }
+    alpha = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun * c2 - mc);
+    rescale = __any(mn != mrun);                   // some row's maximum grew
+    lrun = fmaf(lrun, alpha, lsum);
+    mrun = mn;
+  };
 
-    if (kt + 1 < n_kt) store_tile(buf ^ 1);
-    __syncthreads();
+  // O^T += V^T P^T: A = V^T[32*cb + l32][keys of k-step u, half h2], one
+  // 16-byte read (keys stored contiguously, see vt_pos)
+  const int vt_lane = l32 * C::kVtPitch + h2 * 16;
+  auto pv = [&](const bf16x8_t* pop, const char* sv) {
+    const char* vlane = sv + vt_lane;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      bf16x8_t vop[C::kColBlocks];
+#pragma unroll
+      for (int cb = 0; cb < C::kColBlocks; ++cb)
+        vop[cb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(vlane + (32 * cb) * C::kVtPitch + 32 * u));
+#pragma unroll
+      for (int cb = 0; cb < C::kColBlocks; ++cb) acc[cb] = mfma32(vop[cb], pop[u], acc[cb]);
+    }
+  };
+  auto rescale_acc = [&](float alpha) {
+#pragma unroll
+    for (int cb = 0; cb < C::kColBlocks; ++cb) acc[cb] *= alpha;
+  };
+
+  // Software pipeline over key tiles.  Iteration t issues, as one scheduling
+  // region with no branch inside: the score MFMAs of tile t+1, the weighted
+  // sum of tile t-1 (its weights were made one iteration earlier) and the
+  // softmax of tile t -- independent work for the matrix and the vector unit
+  // of the same wave.  The running output is rescaled (rarely: only when a
+  // row's maximum grew) at the top of the iteration, before tile t-1's weights
+  // are added.  LDS: K slot (t+1)&1 holds K(t+1), V slot (t+1)&1 holds V(t-1);
+  // the global loads of K(t+2) and V(t) land in the slots t&1 this iteration
+  // freed.  Tiles before t_split lie wholly below every row of the workgroup
+  // (no mask) and have a successor; the rest take the masked path.
+  const int t_split = min(n_kt - 1, (qt * rows_wg) / kKT);
+  load_rows(kbase, 0, kreg);
+  store_rows(kslot(0), C::kKPitch, kreg);
+  if (n_kt > 1) {
+    load_rows(kbase, 1, kreg);
+    store_rows(kslot(1), C::kKPitch, kreg);
   }
+  __syncthreads();
+  f32x16_t scur[2], snext[2];
+  qk(kslot(0), scur);
+  bf16x8_t pprev[4];
+  float alpha_prev = 1.f;
+  bool rescale_prev = false;
+
+  // one unmasked iteration (with_pv is a constant at each call site, so the
+  // region below has no branch)
+  auto iter_unmasked = [&](int t, bool with_pv) {
+    if (rescale_prev) rescale_acc(alpha_prev);
+    load_rows(kbase, min(t + 2, n_kt - 1), kreg);
+    load_vpairs(t);
+    qk(kslot((t + 1) & 1), snext);
+    if (with_pv) pv(pprev, vslot((t + 1) & 1));
+    softmax(scur, t * kKT, false, pprev, alpha_prev, rescale_prev);
+    store_rows(kslot(t & 1), C::kKPitch, kreg);    // K(t) was read by the scores of tile t
+    store_vt(vslot(t & 1));                        // V(t-2) was summed at iteration t-1
+    __syncthreads();
+    scur[0] = snext[0];
+    scur[1] = snext[1];
+  };
+  int t = 0;
+  if (t_split > 0) {
+    iter_unmasked(0, false);
+    for (t = 1; t < t_split; ++t) iter_unmasked(t, true);
+  }
+  for (; t < n_kt; ++t) {                          // tiles that reach the diagonal
+    if (rescale_prev) rescale_acc(alpha_prev);
+    if (t + 2 < n_kt) load_rows(kbase, t + 2, kreg);
+    load_vpairs(t);
+    const bool next_active = t + 1 < n_kt && (t + 1) * kKT <= t_base + kQT - 1;
+    if (next_active) qk(kslot((t + 1) & 1), snext);
+    if (t > 0 && (t - 1) * kKT <= t_base + kQT - 1) pv(pprev, vslot((t + 1) & 1));
+    if (t * kKT <= t_base + kQT - 1) {
+      softmax(scur, t * kKT, true, pprev, alpha_prev, rescale_prev);
+    } else {
+      rescale_prev = false;
+    }
+    if (t + 2 < n_kt) store_rows(kslot(t & 1), C::kKPitch, kreg);
+    store_vt(vslot(t & 1));
+    __syncthreads();
+    scur[0] = snext[0];
+    scur[1] = snext[1];
+  }
+  // the last tile's weighted sum
+  if (rescale_prev) rescale_acc(alpha_prev);
+  if ((n_kt - 1) * kKT <= t_base + kQT - 1) pv(pprev, vslot((n_kt - 1) & 1));
 
   const float l = lrun + shfl_xor(lrun, 32);
   if (t_row < p.T) {
@@ -298,17 +385,22 @@ bool prefill_mfma_supports(int n_rep, int d) {
   return (d == 64 || d == 128) && (n_rep == 1 || n_rep == 2 || n_rep % 4 == 0);
 }
 
+#ifndef GQA_PREFILL_WAVES
+#define GQA_PREFILL_WAVES 8
+#endif
+
 hipError_t launch_prefill_mfma(const PrefillProblem& p, hipStream_t stream) {
+  constexpr int NW = GQA_PREFILL_WAVES;
   const int nre = p.n_rep < 4 ? p.n_rep : 4;
-  const int rows_wg = kQT * (4 / nre);
+  const int rows_wg = kQT * (NW / nre);
   const int64_t n_qt = (p.T + rows_wg - 1) / rows_wg;
   const int64_t blocks = n_qt * p.B * p.G * (p.n_rep / nre);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (p.d == 128)
-    hipLaunchKernelGGL(prefill_mfma_kernel<128>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((prefill_mfma_kernel<128, NW>), dim3(unsigned(blocks)), dim3(64 * NW), 0, stream, p);
   else
-    hipLaunchKernelGGL(prefill_mfma_kernel<64>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((prefill_mfma_kernel<64, NW>), dim3(unsigned(blocks)), dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
 }
 
