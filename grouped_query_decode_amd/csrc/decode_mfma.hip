@@ -44,12 +44,22 @@ struct Cfg {
   static constexpr int kColBlocks = D / 16;       // 16-wide output column blocks
   static constexpr int kChunks = D / 8;           // 16-byte chunks per cached row
   static constexpr int kVLoads = kKT * kChunks / 64;
-  static constexpr int kPitch = D * 2 + 16;       // LDS bytes per V row (bank spread)
+  static constexpr int kPitch = D * 2 + 32;       // LDS bytes per V row (transposing reads hit distinct banks)
   static constexpr int kWaveLds = kKT * kPitch;
   static constexpr int kMergeRow = D + 4;         // floats per head row in the merge area
   static constexpr int kMergeBytes = (kMaxWaves * 16 * kMergeRow + 3 * kMaxWaves * 16 + 32) * 4;
   static constexpr int kLds = kMaxWaves * kWaveLds > kMergeBytes ? kMaxWaves * kWaveLds : kMergeBytes;
 };
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): within each 16-lane
+// group, lanes 4e..4e+3 each address 4 consecutive 16-bit values of row e of
+// a 4 x 16 block, and lane i receives column i of the 4 rows.
+__device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(const_cast<char*>(p)));
+}
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -63,6 +73,7 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 // resource returns zeros.
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kDeviceCoherent = 16;    // cache-policy bit sc1
+constexpr int kNonTemporal = 2;        // cache-policy bit nt (streamed once)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
@@ -73,14 +84,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 // their loads (for every item) in flight together; the running maximum is
 // rescaled per batch.
 template <int D, int NI>
-__device__ __forceinline__ void merge_items(const DecodeProblem& p, int b, const int* hs, const int* c8s) {
+__device__ __forceinline__ void merge_items(const DecodeProblem& p, int b, int ns, const int* hs, const int* c8s) {
   const int S = p.num_splits;
   __amdgpu_buffer_rsrc_t rml[NI], ro[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int64_t pr0 = (int64_t(b) * p.H + hs[i]) * S;
-    rml[i] = rsrc(p.part_ml + pr0 * 2, uint32_t(S) * 8u);
-    ro[i] = rsrc(p.part_o + pr0 * D, uint32_t(S) * D * 4u);
+    rml[i] = rsrc(p.part_ml + pr0 * 2, uint32_t(ns) * 8u);
+    ro[i] = rsrc(p.part_o + pr0 * D, uint32_t(ns) * D * 4u);
   }
   float M[NI], L[NI], O[NI][8];
 #pragma unroll
@@ -90,14 +101,14 @@ __device__ __forceinline__ void merge_items(const DecodeProblem& p, int b, const
 #pragma unroll
     for (int e = 0; e < 8; ++e) O[i][e] = 0.f;
   }
-  for (int s0 = 0; s0 < S; s0 += 8) {
+  for (int s0 = 0; s0 < ns; s0 += 8) {
     u32x2_t ml[NI][8];
     u32x4_t oa[NI][8], ob[NI][8];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int s = s0 + u;                      // s >= S reads zeros (l = 0: skipped)
+        const int s = s0 + u;                      // s >= ns reads zeros (l = 0: skipped)
         ml[i][u] = __builtin_amdgcn_raw_buffer_load_b64(rml[i], s * 8, 0, kDeviceCoherent);
         oa[i][u] = __builtin_amdgcn_raw_buffer_load_b128(ro[i], s * D * 4 + c8s[i] * 32, 0, kDeviceCoherent);
         ob[i][u] = __builtin_amdgcn_raw_buffer_load_b128(ro[i], s * D * 4 + c8s[i] * 32 + 16, 0, kDeviceCoherent);
@@ -138,37 +149,49 @@ __device__ __forceinline__ void merge_items(const DecodeProblem& p, int b, const
 }
 
 template <int D>
-__device__ __forceinline__ void merge_splits(const DecodeProblem& p, int b, int h, int c8) {
-  merge_items<D, 1>(p, b, &h, &c8);
+__device__ __forceinline__ void merge_splits(const DecodeProblem& p, int b, int ns, int h, int c8) {
+  merge_items<D, 1>(p, b, ns, &h, &c8);
 }
 
 template <int D>
-__device__ __forceinline__ void merge_splits2(const DecodeProblem& p, int b, int h0, int c0, int h1, int c1) {
+__device__ __forceinline__ void merge_splits2(const DecodeProblem& p, int b, int ns, int h0, int c0, int h1, int c1) {
   const int hs[2] = {h0, h1};
   const int cs[2] = {c0, c1};
-  merge_items<D, 2>(p, b, hs, cs);
+  merge_items<D, 2>(p, b, ns, hs, cs);
 }
 
 template <int D, int NHB>
-__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
+__global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(DecodeProblem p) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::kLds];
   __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int nw = blockDim.x >> 6;
   const int lo = lane & 15;
   const int hi = lane >> 4;
 
+  // Split-major order: consecutive workgroups take the same split of
+  // consecutive (b, g) units.  Workgroups are spread over the XCDs round-robin
+  // by index, so every XCD gets an even share of each split index (with
+  // ragged lengths the late splits are the ones that are often empty), and
+  // the first splits, which are never empty, start first.
   const int S = p.num_splits;
-  const int s = int(blockIdx.x % unsigned(S));
-  const int unit = int(blockIdx.x / unsigned(S));
+  const int units = p.B * p.G;
+  const int s = int(blockIdx.x / unsigned(units));
+  const int unit = int(blockIdx.x % unsigned(units));
   const int g = unit % p.G;
   const int b = unit / p.G;
 
   int len = p.seqlens[b];
   len = len < 0 ? 0 : (len > p.n_max ? p.n_max : len);
+  // Splits that hold positions (at least one, so that an empty sequence still
+  // gets its zero output written).  With the merge inside this launch the
+  // other splits have nothing to do; with the separate merge kernel every
+  // split leaves a (possibly empty) partial.
+  const int ns = p.counters == nullptr ? S : max(1, min(S, (len + p.split_len - 1) / p.split_len));
+  if (s >= ns) return;
   const int j0 = s * p.split_len;
   const int j1 = min(len, j0 + p.split_len);
 
@@ -204,53 +227,49 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
   const float c2 = p.scale * kLog2e;
   char* myv = smem + wave * C::kWaveLds;
 
-  u32x4_t kreg[2][C::kSteps];
-  u32x4_t vreg[C::kVLoads];
-
-  auto load_tile = [&](int jt) {
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int key = jt + 16 * blk + lo;
-#pragma unroll
-      for (int ks = 0; ks < C::kSteps; ++ks) {
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (key < j1) w = ld16_stream(kb + int64_t(key) * D + (4 * ks + hi) * 8);
-        kreg[blk][ks] = w;
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < C::kVLoads; ++t) {
-      const int idx = t * 64 + lane;
-      const int key = jt + idx / C::kChunks;
-      const int ch = idx % C::kChunks;
-      u32x4_t w = {0u, 0u, 0u, 0u};
-      if (key < j1) w = ld16_stream(vb + int64_t(key) * D + ch * 8);
-      vreg[t] = w;
-    }
-  };
-
-  int jt = j0 + wave * kKT;
-  if (jt < j1) load_tile(jt);
-  for (; jt < j1; jt += nw * kKT) {
-    u32x4_t kc[2][C::kSteps];
-    u32x4_t vc[C::kVLoads];
+  // Positions [j0, j1) through buffer resources that end at j1: loads past
+  // the end return zeros without touching memory, so the loads need no
+  // branches and the tile pipeline below has a fixed shape.
+  const int nvalid = j1 > j0 ? j1 - j0 : 0;
+  const uint32_t vbytes = uint32_t(nvalid) * uint32_t(D * 2);
+  const __amdgpu_buffer_rsrc_t rk = rsrc(kb + int64_t(j0) * D, vbytes);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(vb + int64_t(j0) * D, vbytes);
+  // K straight into the score MFMA's A layout: lane (lo, hi) of key block blk,
+  // k-step ks holds row 16*blk + lo, 16-byte chunk 4*ks + hi.  V rows land
+  // 16 bytes per lane, 64 lanes per load covering 64 / kChunks whole rows.
+  const int k_lane = (lo * D + hi * 8) * 2;
+  const int v_lane = lane * 16;
+  typedef u32x4_t KTile[2][C::kSteps];
+  typedef u32x4_t VTile[C::kVLoads];
+  auto load_tile = [&](int tile, KTile& kr, VTile& vr) {
+    const int base = tile * (kKT * D * 2);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int ks = 0; ks < C::kSteps; ++ks) kc[blk][ks] = kreg[blk][ks];
+      for (int ks = 0; ks < C::kSteps; ++ks)
+        kr[blk][ks] = __builtin_amdgcn_raw_buffer_load_b128(rk, base + k_lane + blk * (16 * D * 2) + ks * 64, 0, 0);
 #pragma unroll
-    for (int t = 0; t < C::kVLoads; ++t) vc[t] = vreg[t];
-    if (jt + nw * kKT < j1) load_tile(jt + nw * kKT);
+    for (int t = 0; t < C::kVLoads; ++t)
+      vr[t] = __builtin_amdgcn_raw_buffer_load_b128(rv, base + v_lane + t * 1024, 0, kNonTemporal);
+    // keep each tile's loads together and in program order, so that the
+    // wait before a tile's use covers just the loads issued before it
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-    // V rows of this tile into the wave's LDS area (row-major, padded rows)
+  // V^T operand of the output MFMA by transposing LDS reads: within each
+  // 16-lane group (fixed hi), lanes 4e..4e+3 address row 4*hi + e (4
+  // consecutive dims each) and lane lo receives dim lo of those 4 rows, i.e.
+  // keys 4*hi + e (first read) and 16 + 4*hi + e (second read): exactly the
+  // keys whose weights the lane holds after the score MFMA.
+  const int vt_lane = (4 * hi + (lo >> 2)) * C::kPitch + (lo & 3) * 8;
+
+  auto process = [&](int tile, KTile& kr, VTile& vr) {
+    // V rows of this tile into the wave's LDS area (padded rows)
 #pragma unroll
     for (int t = 0; t < C::kVLoads; ++t) {
       const int idx = t * 64 + lane;
-      const int kl = idx / C::kChunks;
-      const int ch = idx % C::kChunks;
-      *reinterpret_cast<u32x4_t*>(myv + kl * C::kPitch + ch * 16) = vc[t];
+      *reinterpret_cast<u32x4_t*>(myv + (idx / C::kChunks) * C::kPitch + (idx % C::kChunks) * 16) = vr[t];
     }
-
     // scores
     f32x4_t sacc[NHB][2];
 #pragma unroll
@@ -260,11 +279,14 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
         f32x4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < C::kSteps; ++ks)
-          a = mfma16(__builtin_bit_cast(bf16x8_t, kc[blk][ks]), qop[hb][ks], a);
+          a = mfma16(__builtin_bit_cast(bf16x8_t, kr[blk][ks]), qop[hb][ks], a);
         sacc[hb][blk] = a;
       }
+    // this tile's registers are free: fetch the tile after next into them
+    load_tile(tile + 2 * nw, kr, vr);
 
-    // online softmax; lane holds keys jt + 16*blk + 4*hi + r of head lo
+    // online softmax; lane holds keys 16*blk + 4*hi + r of the tile, head lo
+    const int rel0 = tile * kKT + 4 * hi;
     bf16x8_t pop[NHB];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
@@ -274,14 +296,13 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = jt + 16 * blk + 4 * hi + r;
-          const float x = key < j1 ? sacc[hb][blk][r] * c2 : -INFINITY;
+          const float x = rel0 + 16 * blk + r < nvalid ? sacc[hb][blk][r] * c2 : -INFINITY;
           t2[blk][r] = x;
           tmax = fmaxf(tmax, x);
         }
       tmax = fmaxf(tmax, shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-      const float mn = fmaxf(mrun[hb], tmax);      // finite: position jt is valid
+      const float mn = fmaxf(mrun[hb], tmax);      // finite: the tile's first position is valid
       const float alpha = __builtin_amdgcn_exp2f(mrun[hb] - mn);
       mrun[hb] = mn;
       uint32_t w[4];
@@ -303,19 +324,32 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
 
     lds_wave_sync();
     // weighted sum of values
+    const char* vt = myv + vt_lane;
 #pragma unroll
     for (int cb = 0; cb < C::kColBlocks; ++cb) {
-      const int col = 16 * cb + lo;
-      bf16x8_t vop;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kl = 16 * (e >> 2) + 4 * hi + (e & 3);
-        vop[e] = __builtin_bit_cast(__bf16, *reinterpret_cast<const uint16_t*>(myv + kl * C::kPitch + col * 2));
-      }
+      const i16x4_t a4 = lds_read_tr16(vt + cb * 32);
+      const i16x4_t b4 = lds_read_tr16(vt + 16 * C::kPitch + cb * 32);
+      const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, i16x8_t{a4[0], a4[1], a4[2], a4[3], b4[0], b4[1], b4[2], b4[3]});
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) acc[hb][cb] = mfma16(vop, pop[hb], acc[hb][cb]);
     }
-    lds_wave_sync();
+  };
+
+  // Wave w takes tiles w, w + nw, w + 2 nw, ... with two tiles in flight: the
+  // two register sets alternate, so no register copies (and no full wait on
+  // outstanding loads) sit between a tile's loads and its use.
+  const int ntiles = (nvalid + kKT - 1) / kKT;
+  KTile ka, kb2;
+  VTile va, vb2;
+  int tile = wave;
+  load_tile(tile, ka, va);
+  load_tile(tile + nw, kb2, vb2);
+  // (A wave's second tile may lie past the end: all its scores are masked, so
+  // it changes nothing -- the first tile of the pair always has a valid
+  // position, so the running maximum is finite by then.)
+  for (; tile < ntiles; tile += 2 * nw) {
+    process(tile, ka, va);
+    process(tile + nw, kb2, vb2);
   }
 
   // per-head normaliser: the four lanes of a head hold disjoint positions
@@ -365,7 +399,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
         }
       }
       sm_hd[hl] = M;
-      sm_hd[16 + hl] = S == 1 ? (L > 0.f ? 1.f / L : 0.f) : L;
+      sm_hd[16 + hl] = ns == 1 ? (L > 0.f ? 1.f / L : 0.f) : L;
     }
     __syncthreads();
     const int nh = min(16, p.n_rep - 16 * hb);
@@ -377,7 +411,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
       for (int w = 0; w < kMaxWaves; ++w)
         if (w < nw) O += sm_f[w * 16 + hl] * *reinterpret_cast<const f32x4_t*>(sm_o + (w * 16 + hl) * C::kMergeRow + c4 * 4);
       const int h = g * p.n_rep + 16 * hb + hl;
-      if (S == 1) {
+      if (ns == 1) {
         const float inv = sm_hd[16 + hl];
         *reinterpret_cast<uint2*>(p.out + (int64_t(b) * p.H + h) * D + c4 * 4) =
             make_uint2(pack_bf16x2(O[0] * inv, O[1] * inv), pack_bf16x2(O[2] * inv, O[3] * inv));
@@ -395,7 +429,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
       }
     }
   }
-  if (S == 1 || p.counters == nullptr) return;
+  if (ns == 1 || p.counters == nullptr) return;
 
   // Split merge by the last workgroup of this (b, g) to finish.  Each thread
   // waits until its device-coherent partial stores are acknowledged before the
@@ -405,7 +439,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
   __syncthreads();
   if (threadIdx.x == 0) {
     const int old = atomicAdd(p.counters + unit, 1);
-    s_last = (old == S - 1);
+    s_last = (old == ns - 1);
   }
   __syncthreads();
   if (!s_last) return;
@@ -416,11 +450,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeProblem p) {
   const int t0 = threadIdx.x;
   const int t1 = threadIdx.x + blockDim.x;
   if (t1 < items) {
-    merge_splits2<D>(p, b, g * p.n_rep + t0 / kC8, t0 % kC8, g * p.n_rep + t1 / kC8, t1 % kC8);
+    merge_splits2<D>(p, b, ns, g * p.n_rep + t0 / kC8, t0 % kC8, g * p.n_rep + t1 / kC8, t1 % kC8);
     for (int t = t1 + blockDim.x; t < items; t += blockDim.x)
-      merge_splits<D>(p, b, g * p.n_rep + t / kC8, t % kC8);
+      merge_splits<D>(p, b, ns, g * p.n_rep + t / kC8, t % kC8);
   } else if (t0 < items) {
-    merge_splits<D>(p, b, g * p.n_rep + t0 / kC8, t0 % kC8);
+    merge_splits<D>(p, b, ns, g * p.n_rep + t0 / kC8, t0 % kC8);
   }
 }
 
@@ -439,8 +473,11 @@ hipError_t launch_t(const DecodeProblem& p, hipStream_t stream) {
 
 }  // namespace
 
-bool decode_mfma_supports(int n_rep, int d) {
-  return (d == 64 || d == 128) && n_rep >= 1 && n_rep <= 32;
+bool decode_mfma_supports(int n_rep, int d, int split_len) {
+  // a split's bytes, plus the prefetch of up to 2 x 4 tiles past its end,
+  // must fit the buffer instructions' 32-bit offsets
+  const int64_t reach = (int64_t(split_len) + 16 * kKT) * d * 2;
+  return (d == 64 || d == 128) && n_rep >= 1 && n_rep <= 32 && reach < (int64_t(1) << 31);
 }
 
 hipError_t launch_decode_mfma(const DecodeProblem& p, hipStream_t stream) {

@@ -76,7 +76,8 @@ struct MeanpoolProblem {
 // Launchers: each returns hipSuccess or the launch error.
 hipError_t launch_rows_valu(const RowsProblem& p, int dtype, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeProblem& p, hipStream_t stream);
-bool decode_mfma_supports(int n_rep, int d);
+// split_len bounds the 32-bit byte offsets of the kernel's buffer loads
+bool decode_mfma_supports(int n_rep, int d, int split_len);
 hipError_t launch_combine(const CombineProblem& p, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillProblem& p, hipStream_t stream);
 bool prefill_mfma_supports(int n_rep, int d);
