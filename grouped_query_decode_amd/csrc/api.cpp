@@ -152,7 +152,7 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
   const int n_rep = H / G;
 
-  if (dtype == GQA_DTYPE_BF16 && gqa::decode_mfma_supports(n_rep, d, split_len)) {
+  if (dtype == GQA_DTYPE_BF16 && gqa::decode_mfma_supports(n_rep, d, S, split_len)) {
     gqa::DecodeProblem p{};
     p.q = static_cast<const uint16_t*>(q);
     p.k = static_cast<const uint16_t*>(k);

@@ -47,7 +47,7 @@ struct Cfg {
   static constexpr int kPitch = D * 2 + 32;       // LDS bytes per V row (transposing reads hit distinct banks)
   static constexpr int kWaveLds = kKT * kPitch;
   static constexpr int kMergeRow = D + 4;         // floats per head row in the merge area
-  static constexpr int kMergeBytes = (kMaxWaves * 16 * kMergeRow + 3 * kMaxWaves * 16 + 32) * 4;
+  static constexpr int kMergeBytes = (kMaxWaves * 16 * kMergeRow + 2 * kMaxWaves * 16) * 4;
   static constexpr int kLds = kMaxWaves * kWaveLds > kMergeBytes ? kMaxWaves * kWaveLds : kMergeBytes;
 };
 
@@ -79,85 +79,69 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-// Log-sum-exp merge of the S split partials of NI (head, 8-column chunk)
-// items of sequence b, written to out.  Splits are read 8 at a time with all
-// their loads (for every item) in flight together; the running maximum is
+// Split partials of one (b, g) unit: part_o[b][h][s][D] and part_ml[b][h][s][2]
+// for the group's n_rep heads h are contiguous, so one buffer resource --
+// the same for the whole workgroup, as buffer instructions require (a
+// per-lane resource would make the compiler serialise every access over the
+// distinct values) -- covers all of them.
+template <int D>
+struct UnitPartials {
+  __amdgpu_buffer_rsrc_t o, ml;
+  __device__ UnitPartials(const DecodeProblem& p, int b, int g) {
+    const int64_t first = (int64_t(b) * p.H + int64_t(g) * p.n_rep) * p.num_splits;
+    const uint32_t n = uint32_t(p.n_rep) * uint32_t(p.num_splits);
+    o = rsrc(p.part_o + first * D, n * uint32_t(D * 4));
+    ml = rsrc(p.part_ml + first * 2, n * 8u);
+  }
+};
+
+// Log-sum-exp merge of the ns split partials of head hl (within the group)
+// and 8-column chunk c8 of sequence b, written to out.  Splits are read 8 at
+// a time with all their loads in flight together; the running maximum is
 // rescaled per batch.
-template <int D, int NI>
-__device__ __forceinline__ void merge_items(const DecodeProblem& p, int b, int ns, const int* hs, const int* c8s) {
+template <int D>
+__device__ __forceinline__ void merge_item(const DecodeProblem& p, const UnitPartials<D>& up, int b, int ns,
+                                           int h, int hl, int c8) {
   const int S = p.num_splits;
-  __amdgpu_buffer_rsrc_t rml[NI], ro[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int64_t pr0 = (int64_t(b) * p.H + hs[i]) * S;
-    rml[i] = rsrc(p.part_ml + pr0 * 2, uint32_t(ns) * 8u);
-    ro[i] = rsrc(p.part_o + pr0 * D, uint32_t(ns) * D * 4u);
-  }
-  float M[NI], L[NI], O[NI][8];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    M[i] = -INFINITY;
-    L[i] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) O[i][e] = 0.f;
-  }
+  float M = -INFINITY, L = 0.f;
+  f32x4_t Oa = {0.f, 0.f, 0.f, 0.f}, Ob = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
   for (int s0 = 0; s0 < ns; s0 += 8) {
-    u32x2_t ml[NI][8];
-    u32x4_t oa[NI][8], ob[NI][8];
+    u32x2_t ml[8];
+    u32x4_t oa[8], ob[8];
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int s = s0 + u;                      // s >= ns reads zeros (l = 0: skipped)
-        ml[i][u] = __builtin_amdgcn_raw_buffer_load_b64(rml[i], s * 8, 0, kDeviceCoherent);
-        oa[i][u] = __builtin_amdgcn_raw_buffer_load_b128(ro[i], s * D * 4 + c8s[i] * 32, 0, kDeviceCoherent);
-        ob[i][u] = __builtin_amdgcn_raw_buffer_load_b128(ro[i], s * D * 4 + c8s[i] * 32 + 16, 0, kDeviceCoherent);
-      }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float cm = M[i];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (__uint_as_float(ml[i][u][1]) > 0.f) cm = fmaxf(cm, __uint_as_float(ml[i][u][0]));
-      if (cm == -INFINITY) continue;             // nothing seen yet
-      const float f0 = exp2f(M[i] - cm);         // 0 while M is -inf
-      L[i] *= f0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) O[i][e] *= f0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float lu = __uint_as_float(ml[i][u][1]);
-        const float f = lu > 0.f ? exp2f(__uint_as_float(ml[i][u][0]) - cm) : 0.f;
-        L[i] = fmaf(lu, f, L[i]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          O[i][e] = fmaf(__uint_as_float(oa[i][u][e]), f, O[i][e]);
-          O[i][4 + e] = fmaf(__uint_as_float(ob[i][u][e]), f, O[i][4 + e]);
-        }
-      }
-      M[i] = cm;
+    for (int u = 0; u < 8; ++u) {
+      const int pr = hl * S + s0 + u;
+      ml[u] = __builtin_amdgcn_raw_buffer_load_b64(up.ml, pr * 8, 0, kDeviceCoherent);
+      oa[u] = __builtin_amdgcn_raw_buffer_load_b128(up.o, pr * (D * 4) + c8 * 32, 0, kDeviceCoherent);
+      ob[u] = __builtin_amdgcn_raw_buffer_load_b128(up.o, pr * (D * 4) + c8 * 32 + 16, 0, kDeviceCoherent);
     }
-  }
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const float inv = L[i] > 0.f ? 1.f / L[i] : 0.f;
-    u32x4_t w;
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u >= ns) ml[u][1] = 0u;             // not a split of this call: skipped
+    float cm = M;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(O[i][2 * e] * inv, O[i][2 * e + 1] * inv);
-    st16(p.out + (int64_t(b) * p.H + hs[i]) * D + c8s[i] * 8, w);
+    for (int u = 0; u < 8; ++u)
+      if (__uint_as_float(ml[u][1]) > 0.f) cm = fmaxf(cm, __uint_as_float(ml[u][0]));
+    if (cm == -INFINITY) continue;               // nothing seen yet
+    const float f0 = __builtin_amdgcn_exp2f(M - cm);   // 0 while M is -inf
+    L *= f0;
+    Oa *= f0;
+    Ob *= f0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float lu = __uint_as_float(ml[u][1]);
+      const float f = lu > 0.f ? __builtin_amdgcn_exp2f(__uint_as_float(ml[u][0]) - cm) : 0.f;
+      L = fmaf(lu, f, L);
+      Oa += f * __builtin_bit_cast(f32x4_t, oa[u]);
+      Ob += f * __builtin_bit_cast(f32x4_t, ob[u]);
+    }
+    M = cm;
   }
-}
-
-template <int D>
-__device__ __forceinline__ void merge_splits(const DecodeProblem& p, int b, int ns, int h, int c8) {
-  merge_items<D, 1>(p, b, ns, &h, &c8);
-}
-
-template <int D>
-__device__ __forceinline__ void merge_splits2(const DecodeProblem& p, int b, int ns, int h0, int c0, int h1, int c1) {
-  const int hs[2] = {h0, h1};
-  const int cs[2] = {c0, c1};
-  merge_items<D, 2>(p, b, ns, hs, cs);
+  const float inv = L > 0.f ? __builtin_amdgcn_rcpf(L) : 0.f;
+  st16(p.out + (int64_t(b) * p.H + h) * D + c8 * 8,
+       u32x4_t{pack_bf16x2(Oa[0] * inv, Oa[1] * inv), pack_bf16x2(Oa[2] * inv, Oa[3] * inv),
+               pack_bf16x2(Ob[0] * inv, Ob[1] * inv), pack_bf16x2(Ob[2] * inv, Ob[3] * inv)});
 }
 
 template <int D, int NHB>
@@ -361,71 +345,58 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
     lrun[hb] = x;
   }
 
-  // Merge the waves, one head block at a time, and write the output (one
-  // split) or this split's partial result.  One thread per head computes the
-  // merged maximum, the per-wave factors and the normaliser; then every thread
-  // combines 4 output columns of one head.
+  // Merge the waves through LDS, one head block at a time: every wave leaves
+  // its (max, normaliser) per head and its output columns; then each thread
+  // combines 4 columns of one head -- recomputing that head's merged maximum
+  // and per-wave factors itself, which costs a few exps but no serial step
+  // and no extra barrier -- and writes the output (one split) or this
+  // split's partial result.  The code after the main loop runs once per
+  // workgroup, from a cold instruction cache, so it is kept short.
   float* sm_o = reinterpret_cast<float*>(smem);
-  float* sm_m = sm_o + kMaxWaves * 16 * C::kMergeRow;
-  float* sm_l = sm_m + kMaxWaves * 16;
-  float* sm_f = sm_l + kMaxWaves * 16;
-  float* sm_hd = sm_f + kMaxWaves * 16;      // per head: merged max, then normaliser (or 1/it)
+  f32x2_t* sm_ml = reinterpret_cast<f32x2_t*>(sm_o + kMaxWaves * 16 * C::kMergeRow);
   constexpr int kC4 = D / 4;
+  const UnitPartials<D> up(p, b, g);
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     __syncthreads();
 #pragma unroll
     for (int cb = 0; cb < C::kColBlocks; ++cb)
       *reinterpret_cast<f32x4_t*>(sm_o + (wave * 16 + lo) * C::kMergeRow + 16 * cb + 4 * hi) = acc[hb][cb];
-    if (hi == 0) {
-      sm_m[wave * 16 + lo] = mrun[hb];
-      sm_l[wave * 16 + lo] = lrun[hb];
-    }
-    __syncthreads();
-    if (threadIdx.x < 16) {
-      const int hl = threadIdx.x;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kMaxWaves; ++w)
-        if (w < nw && sm_l[w * 16 + hl] > 0.f) M = fmaxf(M, sm_m[w * 16 + hl]);
-      float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < kMaxWaves; ++w) {
-        if (w < nw) {
-          const float lw = sm_l[w * 16 + hl];
-          const float f = lw > 0.f ? exp2f(sm_m[w * 16 + hl] - M) : 0.f;
-          sm_f[w * 16 + hl] = f;
-          L = fmaf(lw, f, L);
-        }
-      }
-      sm_hd[hl] = M;
-      sm_hd[16 + hl] = ns == 1 ? (L > 0.f ? 1.f / L : 0.f) : L;
-    }
+    if (hi == 0) sm_ml[wave * 16 + lo] = f32x2_t{mrun[hb], lrun[hb]};
     __syncthreads();
     const int nh = min(16, p.n_rep - 16 * hb);
     for (int t = threadIdx.x; t < nh * kC4; t += blockDim.x) {
       const int hl = t / kC4;
       const int c4 = t % kC4;
+      f32x2_t ml[kMaxWaves];
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kMaxWaves; ++w) {
+        ml[w] = w < nw ? sm_ml[w * 16 + hl] : f32x2_t{-INFINITY, 0.f};
+        if (ml[w][1] > 0.f) M = fmaxf(M, ml[w][0]);
+      }
+      float L = 0.f;
       f32x4_t O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < kMaxWaves; ++w)
-        if (w < nw) O += sm_f[w * 16 + hl] * *reinterpret_cast<const f32x4_t*>(sm_o + (w * 16 + hl) * C::kMergeRow + c4 * 4);
+      for (int w = 0; w < kMaxWaves; ++w) {
+        if (w < nw) {
+          const float f = ml[w][1] > 0.f ? __builtin_amdgcn_exp2f(ml[w][0] - M) : 0.f;
+          L = fmaf(ml[w][1], f, L);
+          O += f * *reinterpret_cast<const f32x4_t*>(sm_o + (w * 16 + hl) * C::kMergeRow + c4 * 4);
+        }
+      }
       const int h = g * p.n_rep + 16 * hb + hl;
       if (ns == 1) {
-        const float inv = sm_hd[16 + hl];
+        const float inv = L > 0.f ? __builtin_amdgcn_rcpf(L) : 0.f;
         *reinterpret_cast<uint2*>(p.out + (int64_t(b) * p.H + h) * D + c4 * 4) =
             make_uint2(pack_bf16x2(O[0] * inv, O[1] * inv), pack_bf16x2(O[2] * inv, O[3] * inv));
       } else {
-        const int64_t pr = (int64_t(b) * p.H + h) * S + s;
-        const __amdgpu_buffer_rsrc_t ro = rsrc(p.part_o + pr * D, D * 4u);
-        __builtin_amdgcn_raw_buffer_store_b128(
-            u32x4_t{__float_as_uint(O[0]), __float_as_uint(O[1]), __float_as_uint(O[2]), __float_as_uint(O[3])},
-            ro, c4 * 16, 0, kDeviceCoherent);
-        if (c4 == 0) {
-          const __amdgpu_buffer_rsrc_t rml = rsrc(p.part_ml + pr * 2, 8u);
-          __builtin_amdgcn_raw_buffer_store_b64(
-              u32x2_t{__float_as_uint(sm_hd[hl]), __float_as_uint(sm_hd[16 + hl])}, rml, 0, 0, kDeviceCoherent);
-        }
+        const int pr = (16 * hb + hl) * S + s;       // within the unit's partials
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, O), up.o, pr * (D * 4) + c4 * 16, 0,
+                                               kDeviceCoherent);
+        if (c4 == 0)
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(M), __float_as_uint(L)}, up.ml, pr * 8, 0,
+                                                kDeviceCoherent);
       }
     }
   }
@@ -446,16 +417,9 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   if (threadIdx.x == 0)            // ready for the next call (nothing reads it in this one)
     __hip_atomic_store(p.counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   constexpr int kC8 = D / 8;
-  const int items = p.n_rep * kC8;
-  const int t0 = threadIdx.x;
-  const int t1 = threadIdx.x + blockDim.x;
-  if (t1 < items) {
-    merge_splits2<D>(p, b, ns, g * p.n_rep + t0 / kC8, t0 % kC8, g * p.n_rep + t1 / kC8, t1 % kC8);
-    for (int t = t1 + blockDim.x; t < items; t += blockDim.x)
-      merge_splits<D>(p, b, ns, g * p.n_rep + t / kC8, t % kC8);
-  } else if (t0 < items) {
-    merge_splits<D>(p, b, ns, g * p.n_rep + t0 / kC8, t0 % kC8);
-  }
+#pragma unroll 1
+  for (int t = threadIdx.x; t < p.n_rep * kC8; t += blockDim.x)
+    merge_item<D>(p, up, b, ns, g * p.n_rep + t / kC8, t / kC8, t % kC8);
 }
 
 template <int D, int NHB>
@@ -473,11 +437,14 @@ hipError_t launch_t(const DecodeProblem& p, hipStream_t stream) {
 
 }  // namespace
 
-bool decode_mfma_supports(int n_rep, int d, int split_len) {
-  // a split's bytes, plus the prefetch of up to 2 x 4 tiles past its end,
-  // must fit the buffer instructions' 32-bit offsets
+bool decode_mfma_supports(int n_rep, int d, int num_splits, int split_len) {
+  // Byte offsets of the buffer instructions are 32-bit: a split's K/V bytes
+  // (plus the prefetch of up to 2 x 4 tiles past its end) and a unit's
+  // partial results must stay below 2^31.
   const int64_t reach = (int64_t(split_len) + 16 * kKT) * d * 2;
-  return (d == 64 || d == 128) && n_rep >= 1 && n_rep <= 32 && reach < (int64_t(1) << 31);
+  const int64_t partials = int64_t(n_rep) * num_splits * d * 4;
+  return (d == 64 || d == 128) && n_rep >= 1 && n_rep <= 32 && reach < (int64_t(1) << 31) &&
+         partials < (int64_t(1) << 31);
 }
 
 hipError_t launch_decode_mfma(const DecodeProblem& p, hipStream_t stream) {

@@ -76,8 +76,8 @@ struct MeanpoolProblem {
 // Launchers: each returns hipSuccess or the launch error.
 hipError_t launch_rows_valu(const RowsProblem& p, int dtype, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeProblem& p, hipStream_t stream);
-// split_len bounds the 32-bit byte offsets of the kernel's buffer loads
-bool decode_mfma_supports(int n_rep, int d, int split_len);
+// the split geometry bounds the 32-bit byte offsets of the kernel's buffer accesses
+bool decode_mfma_supports(int n_rep, int d, int num_splits, int split_len);
 hipError_t launch_combine(const CombineProblem& p, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillProblem& p, hipStream_t stream);
 bool prefill_mfma_supports(int n_rep, int d);
