@@ -35,16 +35,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Split planning.  The decode kernels run one workgroup per (sequence,
-// K/V head, split).  About two workgroups per compute unit (512 on the 256
-// CUs) are wanted so that every CU streams its share of the cache at once;
-// splits are whole 32-position tiles, at least 128 positions (one tile for each
-// of a workgroup's four waves), which also bounds the merge work of the last
-// workgroup.  Long caches are cut into slices of at
-// most 2048 positions so that ragged lengths balance across the machine.  The
-// partial result of a split (d + 2 floats per head, written and read back
-// once) stays small next to the K/V bytes it covers.
-constexpr int64_t kTargetWorkgroups = 512;
-constexpr int64_t kMinSplitLen = 128;
+// K/V head, split).  About one workgroup per compute unit (256) is wanted so
+// that every CU streams its share of the cache at once; more splits than
+// that cost more in the merge of the partial results (written, counted and
+// read back once per split) than they gain.  Splits are whole 32-position
+// tiles and at least 256 positions long, which bounds the merge work per
+// position; long caches are cut into slices of at most 2048 positions so that
+// ragged lengths balance across the machine.
+constexpr int64_t kTargetWorkgroups = 256;
+constexpr int64_t kMinSplitLen = 256;
 constexpr int64_t kMaxSplitLen = 2048;
 
 bool decode_shape_valid(int B, int H, int G, int d, int n_max) {

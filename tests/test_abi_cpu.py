@@ -108,6 +108,12 @@ def test_split_planner_is_host_only_and_consistent(lib):
         assert ws == lib.gqa_decode_workspace_bytes(B, H, G, d, n, S)
     # long ragged caches are cut into bounded slices
     assert lib.gqa_decode_num_splits(64, 32, 8, 128, 32768) >= 16
+    # about one workgroup per compute unit, splits of at least 256 positions
+    planned = {(16, 32, 32, 128, 1024): 1, (16, 32, 8, 128, 1024): 2, (16, 32, 4, 128, 1024): 4,
+               (16, 32, 1, 128, 1024): 4, (32, 64, 8, 64, 2048): 1, (1, 8, 2, 64, 128): 1,
+               (64, 32, 8, 128, 32768): 16}
+    for shape, S in planned.items():
+        assert lib.gqa_decode_num_splits(*shape) == S, shape
     # forced split counts
     assert lib.gqa_decode_workspace_bytes(1, 8, 2, 64, 128, 1) == 0
     assert lib.gqa_decode_workspace_bytes(1, 8, 2, 64, 128, 7) > 0
