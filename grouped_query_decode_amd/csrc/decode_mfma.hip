@@ -12,22 +12,24 @@
 //   scores  S^T[key][head] = K[key][:] . Q[head][:]     16x16x32 bf16 MFMA,
 //           A = 16 keys x 32 dims straight from HBM (16-byte loads),
 //           B = the group's queries (registers, loaded once)
-//   softmax online, base 2 (hardware exp2), float32; the weights are rounded to bf16 and the
-//           normaliser sums the rounded weights (so constant V is exact)
+//   softmax online, base 2 (hardware exp2), float32; the weights are rounded
+//           to bf16 and the normaliser sums the rounded weights (so constant V
+//           is exact)
 //   output  O^T[dim][head] += V^T[dim][key] P^T[key][head]   16x16x32 MFMA,
-//           A = V^T gathered from a per-wave LDS copy of the 32-row V tile,
-//           B = the weights, already in the right lanes after the scores
+//           A = V^T read with transposing LDS loads from a per-wave copy of
+//           the 32-row V tile, B = the weights, already in the right lanes
+//           after the scores
 //
 // Each wave walks its own 32-position tiles of the split (tile t goes to wave
-// t mod waves) with a one-tile register prefetch; the waves merge (max, sum,
-// output) through LDS.  With several splits, each workgroup writes its
-// partial (max, sum, output) per head; the last workgroup of a (b, g) to
-// finish -- found with a counter in the workspace header, which it resets --
-// merges the partials (log-sum-exp) and writes the output, so one launch does
-// the whole step.  Positions at or beyond the sequence length are never
-// loaded: their K rows are zero, their scores are set to -inf before the
-// softmax and their V rows are zero, so cache contents there (NaN included)
-// cannot reach the arithmetic.
+// t mod waves) with two tiles in flight in alternating register sets; the
+// waves merge (max, sum, output) through LDS.  With several splits, each
+// workgroup writes its partial (max, sum, output) per head; the last workgroup
+// of a (b, g) to finish -- found with a counter in the workspace header, which
+// it resets -- merges the partials (log-sum-exp) and writes the output, so one
+// launch does the whole step.  Positions at or beyond the sequence length are
+// never loaded (the buffer loads end there and return zeros): their K rows are
+// zero, their scores are set to -inf before the softmax and their V rows are
+// zero, so cache contents there (NaN included) cannot reach the arithmetic.
 
 #include "device_common.h"
 #include "internal.h"

@@ -5,11 +5,11 @@
 // CSDN blog: the context phase runs in parallel over the prompt, each position
 // seeing only its past; GQA paper section 2.2 for the grouping).
 //
-// Work unit: one workgroup of 4 waves per (b, g, head quad, query tile).  Each
-// wave owns 32 query positions of one head; the 4 waves of a workgroup are the
-// 4 heads of one group (n_rep >= 4) or 2/4 consecutive 32-position blocks of
-// the group's heads (n_rep = 2/1), so every K/V tile staged in LDS is used by
-// 128 query rows.  Per 64-key tile and wave:
+// Work unit: one workgroup of 8 waves per (b, g, head quad, query tile).  Each
+// wave owns 32 query positions of one head; the waves of a workgroup cover 4
+// heads of one group x 2 consecutive 32-position blocks (n_rep >= 4), or 2
+// heads x 4 blocks (n_rep = 2), or 1 head x 8 blocks (n_rep = 1), so every
+// K/V tile staged in LDS is used by 256 query rows.  Per 64-key tile and wave:
 //
 //   S^T[key][row] = K[key][:] . Q[row][:]        32x32x16 bf16 MFMA (2 x 8),
 //                   A = K tile from LDS, B = the wave's queries (registers)
@@ -19,10 +19,11 @@
 //                   A = V^T from LDS (transposed once per workgroup when the
 //                   tile is staged), B = the bf16 weights, already in place
 //
-// K/V tiles are double-buffered in LDS (row-major, rows padded so that the
-// operand reads hit distinct banks): the next tile's
-// global loads are issued before the current tile's math and land in the other
-// buffer afterwards, one barrier per tile.  Softmax work per score: one FMA
+// K/V tiles are double-buffered in LDS (layouts below): the next tiles'
+// global loads are issued before the current tile's math and land in the freed
+// buffers afterwards, one barrier per tile; the weighted sum of a tile is
+// deferred by one iteration so that each iteration hands the matrix unit and
+// the vector unit independent work.  Softmax work per score: one FMA
 // (scale folded in), one hardware exp2 (weights below 2^-126 may flush to
 // zero), a third of a max3, half a bf16 pack, half a
 // bf16 dot2 for the normaliser (which sums the rounded weights); the running
@@ -40,7 +41,6 @@ constexpr int kKT = 64;     // keys per tile
 constexpr int kQT = 32;     // query positions per wave
 constexpr int kXcds = 8;
 
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 // LDS tiles (64 banks of 4 bytes):
 //  * K row-major, rows padded by 16 bytes: 16 consecutive rows read at one
@@ -385,12 +385,8 @@ bool prefill_mfma_supports(int n_rep, int d) {
   return (d == 64 || d == 128) && (n_rep == 1 || n_rep == 2 || n_rep % 4 == 0);
 }
 
-#ifndef GQA_PREFILL_WAVES
-#define GQA_PREFILL_WAVES 8
-#endif
-
 hipError_t launch_prefill_mfma(const PrefillProblem& p, hipStream_t stream) {
-  constexpr int NW = GQA_PREFILL_WAVES;
+  constexpr int NW = 8;                            // waves per workgroup
   const int nre = p.n_rep < 4 ? p.n_rep : 4;
   const int rows_wg = kQT * (NW / nre);
   const int64_t n_qt = (p.T + rows_wg - 1) / rows_wg;
