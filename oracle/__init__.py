@@ -14,6 +14,8 @@ from .gqa_oracle import (  # noqa: F401
     softmax_weights,
     attend_one_query,
     decode_ref,
+    append_position,
+    decode_append_ref,
     future_keys,
     prefill_causal_ref,
     meanpool_ref,

@@ -36,6 +36,11 @@ Readings taken where the pages are silent (each is also listed in the design doc):
   new k, v onto the cache before the attention), so a sequence of length n
   attends positions 0 .. n-1.  n = 0 gives a zero output; n > Nmax is clamped.
 * Causal prefill: query position i attends keys 0 .. i inclusive.
+* Decode with append: the new token's k, v go to cache position seqlens[b]-1
+  (the length already counts the new token, as above), then the step attends
+  0 .. seqlens[b]-1.  A length of 0 has no position for the token and a length
+  above Nmax points past the cache: in both cases nothing is written (the
+  attention itself then follows the decode rules above).
 * Mean-pooling is the arithmetic mean of the group's member heads.
 
 Pins: every function here is checked against something other than itself
@@ -54,6 +59,8 @@ __all__ = [
     "softmax_weights",
     "attend_one_query",
     "decode_ref",
+    "append_position",
+    "decode_append_ref",
     "future_keys",
     "prefill_causal_ref",
     "meanpool_ref",
@@ -165,6 +172,47 @@ def decode_ref(q, k_cache, v_cache, seqlens, scale: float) -> np.ndarray:
                 continue
             out[b, h] = attend_one_query(q[b, h], k_cache[b, g, :n], v_cache[b, g, :n], scale)
     return out
+
+
+def append_position(seqlen: int, n_max: int):
+    """Cache position that receives the new token's k and v, or None.
+
+    The blog's "KV Cache" section concatenates the current step's k and v onto
+    the cached K and V before the attention; with a cache of Nmax slots and a
+    length that counts the new token, that is slot ``seqlen - 1``.  A length
+    of 0 (no token) or above Nmax (no such slot) writes nothing.
+    """
+    seqlen = int(seqlen)
+    if seqlen < 1 or seqlen > n_max:
+        return None
+    return seqlen - 1
+
+
+def decode_append_ref(q, k_new, v_new, k_cache, v_cache, seqlens, scale: float):
+    """Append the new token's k, v to the cache, then one decode step (float64).
+
+    q: [B, H, d]; k_new, v_new: [B, G, d]; k_cache, v_cache: [B, G, Nmax, d].
+    Returns (out [B, H, d], k_cache after, v_cache after); the inputs are not
+    modified.  Blog "KV Cache" section: K = cat(K_prev, k), V = cat(V_prev, v),
+    then softmax(q.K / sqrt(d)) V over the grown cache.
+    """
+    k_after = np.array(k_cache, dtype=np.float64, copy=True)
+    v_after = np.array(v_cache, dtype=np.float64, copy=True)
+    k_new = np.asarray(k_new, dtype=np.float64)
+    v_new = np.asarray(v_new, dtype=np.float64)
+    seqlens = np.asarray(seqlens).reshape(-1)
+    B, G, n_max, d = k_after.shape
+    if k_new.shape != (B, G, d) or v_new.shape != (B, G, d) or seqlens.shape[0] != B:
+        raise ValueError("inconsistent append shapes")
+    for b in range(B):
+        pos = append_position(seqlens[b], n_max)
+        if pos is None:
+            continue
+        for g in range(G):
+            k_after[b, g, pos] = k_new[b, g]
+            v_after[b, g, pos] = v_new[b, g]
+    out = decode_ref(q, k_after, v_after, seqlens, scale)
+    return out, k_after, v_after
 
 
 def future_keys(rows, T: int) -> np.ndarray:

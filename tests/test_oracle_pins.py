@@ -315,6 +315,66 @@ def pin_meanpool(seed=13):
     assert np.array_equal(oracle.meanpool_ref(marks, 2)[:, 0], [0.0, 1.0])
 
 
+def pin_append_vs_sdpa_concat(seed=15):
+    """Blog "KV Cache": K = cat(K_prev, k), V = cat(V_prev, v), then the attention
+    over the grown cache -- built with torch.cat and run through SDPA (float64)."""
+    rng = _rng(seed)
+    B, H, G, d, n_max = 4, 8, 2, 16, 9
+    scale = 1.0 / math.sqrt(d)
+    q = rng.standard_normal((B, H, d))
+    kc = rng.standard_normal((B, G, n_max, d))
+    vc = rng.standard_normal((B, G, n_max, d))
+    k_new = rng.standard_normal((B, G, d))
+    v_new = rng.standard_normal((B, G, d))
+    seqlens = [1, 5, 9, 3]
+    out, _, _ = oracle.decode_append_ref(q, k_new, v_new, kc, vc, seqlens, scale)
+    for b in range(B):
+        n = seqlens[b]
+        K = torch.cat([torch.from_numpy(kc[b, :, :n - 1]), torch.from_numpy(k_new[b])[:, None]], dim=1)
+        V = torch.cat([torch.from_numpy(vc[b, :, :n - 1]), torch.from_numpy(v_new[b])[:, None]], dim=1)
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q[b])[None, :, None], K[None], V[None],
+                                             scale=scale, enable_gqa=True)[0, :, 0]
+        np.testing.assert_allclose(out[b], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def pin_append_cache_rows(seed=16):
+    """The new k, v land in slot seqlens[b]-1; no other slot changes (NaN stays NaN);
+    a length of 0 or above Nmax writes nothing."""
+    rng = _rng(seed)
+    B, H, G, d, n_max = 5, 4, 2, 8, 6
+    kc = rng.standard_normal((B, G, n_max, d))
+    kc[:, :, 4:] = np.nan
+    vc = kc * 2.0
+    k_new = rng.standard_normal((B, G, d))
+    v_new = rng.standard_normal((B, G, d))
+    seqlens = [3, 1, 6, 0, 7]
+    q = rng.standard_normal((B, H, d))
+    _, ka, va = oracle.decode_append_ref(q, k_new, v_new, kc, vc, seqlens, 0.5)
+    for b, n in enumerate(seqlens):
+        for g in range(G):
+            for j in range(n_max):
+                if 1 <= n <= n_max and j == n - 1:
+                    assert np.array_equal(ka[b, g, j], k_new[b, g]) and np.array_equal(va[b, g, j], v_new[b, g])
+                else:
+                    assert np.array_equal(ka[b, g, j], kc[b, g, j], equal_nan=True)
+                    assert np.array_equal(va[b, g, j], vc[b, g, j], equal_nan=True)
+
+
+def pin_append_single_token(seed=17):
+    """Length 1: the only attended key is the new one, so every head returns its
+    group's new v exactly (whatever the cache holds)."""
+    rng = _rng(seed)
+    B, H, G, d, n_max = 2, 6, 3, 5, 4
+    q = rng.standard_normal((B, H, d))
+    kc = np.full((B, G, n_max, d), np.nan)
+    k_new = rng.standard_normal((B, G, d))
+    v_new = rng.standard_normal((B, G, d))
+    out, _, _ = oracle.decode_append_ref(q, k_new, v_new, kc, kc, [1, 1], 0.3)
+    for b in range(B):
+        for h in range(H):
+            assert np.array_equal(out[b, h], v_new[b, h // (H // G)])
+
+
 def pin_flop_counts():
     # Decode operations do not depend on G (blog, "MQA 的推导": the arithmetic is unchanged)
     assert oracle.decode_flops(32, 16 * 1024, 128) == 268435456
@@ -329,7 +389,7 @@ PINS = [
     pin_mqa_vs_sdpa_broadcast, pin_brute_force, pin_single_key, pin_constant_values,
     pin_zero_query_is_mean, pin_two_keys_sigmoid, pin_repeat_kv, pin_tail_ignored,
     pin_permutation, pin_prefill_vs_sdpa, pin_prefill_rows_are_decodes, pin_meanpool,
-    pin_flop_counts,
+    pin_append_vs_sdpa_concat, pin_append_cache_rows, pin_append_single_token, pin_flop_counts,
 ]
 
 
@@ -434,3 +494,15 @@ def test_mutation_meanpool_sum_caught(monkeypatch):
     orig = og.meanpool_ref
     monkeypatch.setattr(oracle, "meanpool_ref", lambda w, G: orig(w, G) * (np.asarray(w).shape[0] // G))
     assert _fails([pin_meanpool]) == ["pin_meanpool"]
+
+
+def test_mutation_append_off_by_one_caught(monkeypatch):
+    monkeypatch.setattr(og, "append_position", lambda s, n: int(s) if 0 <= int(s) < n else None)
+    failed = _fails([pin_append_vs_sdpa_concat, pin_append_cache_rows, pin_append_single_token])
+    assert "pin_append_vs_sdpa_concat" in failed and "pin_append_cache_rows" in failed
+
+
+def test_mutation_append_skipped_caught(monkeypatch):
+    monkeypatch.setattr(og, "append_position", lambda s, n: None)
+    failed = _fails([pin_append_vs_sdpa_concat, pin_append_cache_rows, pin_append_single_token])
+    assert len(failed) == 3
