@@ -7,6 +7,7 @@ PyTorch stream is passed to the library.  There is no fallback: if the
 library is missing, every call raises.
 
     decode(q, k_cache, v_cache, seqlens)        # one decode step, [B,H,d]
+    decode_append(q, k_new, v_new, k_cache, v_cache, seqlens)  # append, then decode
     prefill_causal(q, k, v)                     # causal prefill, [B,T,H,d]
     meanpool_heads(w, G)                        # MHA -> GQA K/V conversion
 """
@@ -20,7 +21,7 @@ import os
 import torch
 
 __all__ = [
-    "GQAError", "library_path", "load_library", "decode", "decode_num_splits",
+    "GQAError", "library_path", "load_library", "decode", "decode_append", "decode_num_splits",
     "decode_workspace_bytes", "prefill_causal", "meanpool_heads", "DTYPE_CODES",
 ]
 
@@ -66,6 +67,9 @@ def load_library():
     lib.gqa_decode_split.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32,
                                      vp, sz, vp]
     lib.gqa_decode_split.restype = i32
+    lib.gqa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+                                      i32, vp, sz, vp]
+    lib.gqa_decode_append.restype = i32
     lib.gqa_prefill_causal.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.gqa_prefill_causal.restype = i32
     lib.kv_meanpool_heads.argtypes = [vp, vp, i32, i32, i64, i32, vp]
@@ -175,6 +179,51 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlen
                               B, H, G, d, n_max, float(scale), _dtype_code(q), int(num_splits),
                               _ptr(workspace), ws_bytes, ctypes.c_void_p(_stream_handle(dev)))
     _check("gqa_decode", st)
+    return out
+
+
+def decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                  v_cache: torch.Tensor, seqlens: torch.Tensor, scale: float | None = None,
+                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                  num_splits: int = 0) -> torch.Tensor:
+    """Append this step's k, v (k_new, v_new [B,G,d]) at slot seqlens[b]-1 of the
+    caches (in place), then one decode step; see :func:`decode` for the rest."""
+    lib = load_library()
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B,H,d] and k_cache [B,G,Nmax,d]")
+    B, H, d = q.shape
+    Bk, G, n_max, dk = k_cache.shape
+    if (Bk, dk) != (B, d) or v_cache.shape != k_cache.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k_cache.shape)}, "
+                         f"v {tuple(v_cache.shape)}")
+    if k_new.shape != (B, G, d) or v_new.shape != (B, G, d):
+        raise ValueError("k_new and v_new must be [B,G,d]")
+    for t in (k_cache, v_cache, k_new, v_new):
+        if t.dtype != q.dtype:
+            raise TypeError("all tensors must share q's dtype")
+    if seqlens.dtype != torch.int32 or seqlens.shape != (B,):
+        raise ValueError("seqlens must be an int32 tensor of shape [B]")
+    dev = q.device
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                    ("v_cache", v_cache), ("seqlens", seqlens)):
+        _require_device(name, t, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require_device("out", out, dev)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_bytes(B, H, G, d, n_max, num_splits) if B > 0 else 0
+    if need > 0 and workspace is None:
+        workspace = _cached_workspace(dev, need)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gqa_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(seqlens), _ptr(out), B, H, G, d, n_max, float(scale),
+                               _dtype_code(q), int(num_splits), _ptr(workspace), ws_bytes,
+                               ctypes.c_void_p(_stream_handle(dev)))
+    _check("gqa_decode_append", st)
     return out
 
 

@@ -105,8 +105,10 @@ gqa_status launched(hipError_t e, const char* what) {
 
 gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_t* seqlens,
                        void* out, int B, int H, int G, int d, int n_max, float scale, int dtype,
-                       int num_splits, void* ws, size_t ws_bytes, void* stream_v) {
+                       int num_splits, void* ws, size_t ws_bytes, void* stream_v,
+                       const void* k_new = nullptr, const void* v_new = nullptr) {
   g_last_error.clear();
+  const bool append = k_new != nullptr || v_new != nullptr;
   if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
     return fail(GQA_ERR_INVALID_ARG, "gqa_decode: unknown dtype %d", dtype);
   if (B < 0 || n_max < 0)
@@ -119,8 +121,10 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
   if (d < 1) return fail(GQA_ERR_INVALID_ARG, "gqa_decode: head size d=%d", d);
   if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "gqa_decode: scale is not finite");
   if (num_splits < 0) return fail(GQA_ERR_INVALID_ARG, "gqa_decode: num_splits=%d", num_splits);
-  if (!q || !out || !seqlens || (n_max > 0 && (!k || !v)))
+  if (!q || !out || !seqlens || (n_max > 0 && (!k || !v)) || (append && (!k_new || !v_new)))
     return fail(GQA_ERR_INVALID_ARG, "gqa_decode: NULL tensor pointer");
+  if (append && (!aligned16(k_new) || !aligned16(v_new)))
+    return fail(GQA_ERR_INVALID_ARG, "gqa_decode: tensors must be 16-byte aligned");
   if (!aligned16(q) || !aligned16(out) || (n_max > 0 && (!aligned16(k) || !aligned16(v))) ||
       (reinterpret_cast<uintptr_t>(seqlens) & 3u))
     return fail(GQA_ERR_INVALID_ARG, "gqa_decode: tensors must be 16-byte aligned");
@@ -162,6 +166,8 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
     p.part_ml = part_ml;
     // the split merge runs inside the decode kernel when the counters fit
     p.counters = (S > 1 && int64_t(B) * G <= kMaxCountedUnits) ? counters : nullptr;
+    p.k_new = static_cast<const uint16_t*>(k_new);
+    p.v_new = static_cast<const uint16_t*>(v_new);
     p.B = B; p.H = H; p.G = G; p.n_rep = n_rep; p.d = d; p.n_max = n_max;
     p.scale = scale;
     p.num_splits = S;
@@ -169,6 +175,15 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
     gqa_status st = launched(gqa::launch_decode_mfma(p, stream), "gqa_decode");
     if (st != GQA_OK || S == 1 || p.counters != nullptr) return st;
   } else {
+    if (append && n_max > 0) {
+      // float32 path: the new rows go in first (same stream, so the decode sees them)
+      gqa::AppendProblem a{};
+      a.k_new = k_new; a.v_new = v_new; a.k = const_cast<void*>(k); a.v = const_cast<void*>(v);
+      a.seqlens = seqlens; a.B = B; a.G = G; a.n_max = n_max;
+      a.row_bytes = d * (dtype == GQA_DTYPE_F32 ? 4 : 2);
+      gqa_status st = launched(gqa::launch_append(a, stream), "gqa_decode_append (append)");
+      if (st != GQA_OK) return st;
+    }
     gqa::RowsProblem p{};
     p.q = q; p.k = k; p.v = v; p.seqlens = seqlens; p.out = out;
     p.part_o = part_o; p.part_ml = part_ml;
@@ -228,6 +243,18 @@ gqa_status gqa_decode_split(const void* q, const void* k_cache, const void* v_ca
                             size_t workspace_bytes, void* stream) {
   return decode_impl(q, k_cache, v_cache, seqlens, out, B, H, G, d, n_max, scale, dtype,
                      num_splits, workspace, workspace_bytes, stream);
+}
+
+gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                             void* v_cache, const int32_t* seqlens, void* out, int B, int H, int G,
+                             int d, int n_max, float scale, int dtype, int num_splits,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (B > 0 && (!k_new || !v_new)) {
+    g_last_error.clear();
+    return fail(GQA_ERR_INVALID_ARG, "gqa_decode_append: NULL k_new / v_new");
+  }
+  return decode_impl(q, k_cache, v_cache, seqlens, out, B, H, G, d, n_max, scale, dtype,
+                     num_splits, workspace, workspace_bytes, stream, k_new, v_new);
 }
 
 gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void* out, int B,

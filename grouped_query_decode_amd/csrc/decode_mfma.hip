@@ -170,8 +170,8 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   const int g = unit % p.G;
   const int b = unit / p.G;
 
-  int len = p.seqlens[b];
-  len = len < 0 ? 0 : (len > p.n_max ? p.n_max : len);
+  const int raw_len = p.seqlens[b];
+  const int len = raw_len < 0 ? 0 : (raw_len > p.n_max ? p.n_max : raw_len);
   // Splits that hold positions (at least one, so that an empty sequence still
   // gets its zero output written).  With the merge inside this launch the
   // other splits have nothing to do; with the separate merge kernel every
@@ -184,6 +184,22 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   const int64_t kv_off = (int64_t(b) * p.G + g) * int64_t(p.n_max) * D;
   const uint16_t* kb = p.k + kv_off;
   const uint16_t* vb = p.v + kv_off;
+
+  // Append (when k_new is given): the new token's k, v belong in slot
+  // raw_len-1 if that slot exists.  The split holding that slot writes them
+  // to the cache and attends them straight from a copy in LDS (no other
+  // workgroup reads that slot in this launch); its stream of cached rows
+  // stops just before the slot.
+  __shared__ __attribute__((aligned(16))) char s_new[2 * D * 2];
+  const int p_new = (p.k_new != nullptr && raw_len >= 1 && raw_len <= p.n_max) ? raw_len - 1 : -1;
+  const bool owner = p_new >= j0 && p_new < j1;
+  if (owner && threadIdx.x < 2 * C::kChunks) {
+    const int c = threadIdx.x % C::kChunks;
+    const bool is_v = threadIdx.x >= C::kChunks;
+    const u32x4_t w = ld16((is_v ? p.v_new : p.k_new) + (int64_t(b) * p.G + g) * D + c * 8);
+    st16(const_cast<uint16_t*>(is_v ? vb : kb) + int64_t(p_new) * D + c * 8, w);
+    *reinterpret_cast<u32x4_t*>(s_new + (is_v ? D * 2 : 0) + c * 16) = w;
+  }
 
   // Queries of the group: B operand of the score MFMA, lane = head lo of head
   // block hb, k-slot group hi covers dims 8*(4*ks + hi) .. +7.
@@ -216,7 +232,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   // Positions [j0, j1) through buffer resources that end at j1: loads past
   // the end return zeros without touching memory, so the loads need no
   // branches and the tile pipeline below has a fixed shape.
-  const int nvalid = j1 > j0 ? j1 - j0 : 0;
+  const int nvalid = owner ? p_new - j0 : (j1 > j0 ? j1 - j0 : 0);
   const uint32_t vbytes = uint32_t(nvalid) * uint32_t(D * 2);
   const __amdgpu_buffer_rsrc_t rk = rsrc(kb + int64_t(j0) * D, vbytes);
   const __amdgpu_buffer_rsrc_t rv = rsrc(vb + int64_t(j0) * D, vbytes);
@@ -249,7 +265,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   // keys whose weights the lane holds after the score MFMA.
   const int vt_lane = (4 * hi + (lo >> 2)) * C::kPitch + (lo & 3) * 8;
 
-  auto process = [&](int tile, KTile& kr, VTile& vr) {
+  auto process = [&](int tile, KTile& kr, VTile& vr, int nv, bool prefetch) {
     // V rows of this tile into the wave's LDS area (padded rows)
 #pragma unroll
     for (int t = 0; t < C::kVLoads; ++t) {
@@ -269,7 +285,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
         sacc[hb][blk] = a;
       }
     // this tile's registers are free: fetch the tile after next into them
-    load_tile(tile + 2 * nw, kr, vr);
+    if (prefetch) load_tile(tile + 2 * nw, kr, vr);
 
     // online softmax; lane holds keys 16*blk + 4*hi + r of the tile, head lo
     const int rel0 = tile * kKT + 4 * hi;
@@ -282,7 +298,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float x = rel0 + 16 * blk + r < nvalid ? sacc[hb][blk][r] * c2 : -INFINITY;
+          const float x = rel0 + 16 * blk + r < nv ? sacc[hb][blk][r] * c2 : -INFINITY;
           t2[blk][r] = x;
           tmax = fmaxf(tmax, x);
         }
@@ -334,8 +350,29 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   // it changes nothing -- the first tile of the pair always has a valid
   // position, so the running maximum is finite by then.)
   for (; tile < ntiles; tile += 2 * nw) {
-    process(tile, ka, va);
-    process(tile + nw, kb2, vb2);
+    process(tile, ka, va, nvalid, true);
+    process(tile + nw, kb2, vb2, nvalid, true);
+  }
+  if (owner) {
+    // the appended token, as a one-row tile on wave 0 (its k, v from LDS)
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int ks = 0; ks < C::kSteps; ++ks) {
+          u32x4_t w = {0u, 0u, 0u, 0u};
+          if (blk == 0 && lo == 0) w = *reinterpret_cast<const u32x4_t*>(s_new + (4 * ks + hi) * 16);
+          ka[blk][ks] = w;
+        }
+#pragma unroll
+      for (int t = 0; t < C::kVLoads; ++t) {
+        u32x4_t w = {0u, 0u, 0u, 0u};
+        if (t == 0 && lane < C::kChunks) w = *reinterpret_cast<const u32x4_t*>(s_new + D * 2 + lane * 16);
+        va[t] = w;
+      }
+      process(0, ka, va, 1, false);
+    }
   }
 
   // per-head normaliser: the four lanes of a head hold disjoint positions

@@ -43,6 +43,8 @@ struct DecodeProblem {
   float* part_o;
   float* part_ml;
   int* counters;            // [B*G] split-arrival counters (zero between calls), or null
+  const uint16_t* k_new;    // [B, G, d] this step's k, v to append at seqlens[b]-1, or null
+  const uint16_t* v_new;
   int B, H, G, n_rep, d, n_max;
   float scale;
   int num_splits, split_len;
@@ -65,6 +67,18 @@ struct PrefillProblem {
   float scale;
 };
 
+// Write this step's k, v rows into the caches at position seqlens[b]-1
+// (when 1 <= seqlens[b] <= n_max), any element type.
+struct AppendProblem {
+  const void* k_new;        // [B, G, row_bytes]
+  const void* v_new;
+  void* k;                  // [B, G, n_max, row_bytes]
+  void* v;
+  const int32_t* seqlens;
+  int B, G, n_max;
+  int row_bytes;            // d * itemsize, a multiple of 16
+};
+
 struct MeanpoolProblem {
   const void* w_in;
   void* w_out;
@@ -79,6 +93,7 @@ hipError_t launch_decode_mfma(const DecodeProblem& p, hipStream_t stream);
 // the split geometry bounds the 32-bit byte offsets of the kernel's buffer accesses
 bool decode_mfma_supports(int n_rep, int d, int num_splits, int split_len);
 hipError_t launch_combine(const CombineProblem& p, hipStream_t stream);
+hipError_t launch_append(const AppendProblem& p, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillProblem& p, hipStream_t stream);
 bool prefill_mfma_supports(int n_rep, int d);
 hipError_t launch_meanpool(const MeanpoolProblem& p, hipStream_t stream);

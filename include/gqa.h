@@ -133,6 +133,37 @@ gqa_status gqa_decode_split(const void* q, const void* k_cache, const void* v_ca
                             void* stream);
 
 /*
+ * gqa_decode_append - append this step's k, v to the caches, then decode, in
+ * one call (one kernel launch on the bfloat16 path).
+ *
+ * Defines (the fogdragon CSDN blog, section "KV Cache": each step
+ * concatenates its new k and v onto the cached K and V -- K = cat(K_prev, k),
+ * V = cat(V_prev, v) -- and then attends the grown cache):
+ *
+ *   if 1 <= seqlens[b] <= n_max:
+ *       k_cache[b,g,seqlens[b]-1,:] = k_new[b,g,:];  v_cache[...] = v_new[b,g,:]
+ *   then out = gqa_decode(q, k_cache, v_cache, seqlens)  (same definition).
+ *
+ *   k_new, v_new  [B, G, d]        dtype, device, read only.
+ *   k_cache, v_cache [B, G, n_max, d]  dtype, device; exactly the row
+ *                  seqlens[b]-1 of each (b, g) is written (a copy of the new
+ *                  row, bit for bit); nothing is written for a length of 0
+ *                  (no token) or above n_max (no such slot), and those
+ *                  sequences decode as gqa_decode would.  Every other cache
+ *                  element is left untouched.
+ *   num_splits     as in gqa_decode_split (0 = the planner's choice).
+ *   Other arguments, workspace contract and errors: as gqa_decode_split;
+ *   k_new or v_new NULL (with B > 0) or misaligned is GQA_ERR_INVALID_ARG.
+ *   The result equals writing the rows and then calling gqa_decode, up to the
+ *   order of the floating-point sums.
+ */
+gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, const int32_t* seqlens, void* out,
+                             int B, int H, int G, int d, int n_max, float scale, int dtype,
+                             int num_splits, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * gqa_prefill_causal - causal GQA over whole prompts (the context phase).
  *
  * The blog's decoder discussion: the prompt is processed in parallel like an

@@ -29,6 +29,7 @@ __all__ = [
     "WORKLOADS",
     "scale_for",
     "decode_inputs",
+    "decode_append_inputs",
     "prefill_inputs",
     "meanpool_inputs",
     "to_f64",
@@ -134,6 +135,20 @@ def decode_inputs(B, H, G, d, n_max, dtype="bf16", seed=0, device="cpu", seqlens
         k.masked_fill_(tail, float("nan"))
         v.masked_fill_(tail, float("nan"))
     return {"q": q, "k_cache": k, "v_cache": v, "seqlens": sl}
+
+
+def decode_append_inputs(B, H, G, d, n_max, dtype="bf16", seed=0, device="cpu", seqlens="full",
+                         nan_tail=False, std=1.0):
+    """decode_inputs(...) plus this step's k_new, v_new [B,G,d], drawn after them
+    from a generator of seed + 1_000_003 (so q and the caches match decode_inputs
+    of the same seed)."""
+    x = decode_inputs(B, H, G, d, n_max, dtype=dtype, seed=seed, device=device, seqlens=seqlens,
+                      nan_tail=nan_tail, std=std)
+    dt = x["q"].dtype
+    gen = _gen(device, seed + 1_000_003)
+    x["k_new"] = _randn((B, G, d), gen, device, std, dt)
+    x["v_new"] = _randn((B, G, d), gen, device, std, dt)
+    return x
 
 
 def prefill_inputs(B, T, H, G, d, dtype="bf16", seed=0, device="cpu", std=0.5):

@@ -34,7 +34,8 @@ def lib():
 
 def test_header_declares_the_api():
     names = declared_functions()
-    for n in ("gqa_decode", "gqa_decode_split", "gqa_prefill_causal", "kv_meanpool_heads",
+    for n in ("gqa_decode", "gqa_decode_split", "gqa_decode_append", "gqa_prefill_causal",
+              "kv_meanpool_heads",
               "gqa_decode_workspace_bytes", "gqa_decode_num_splits", "gqa_status_string",
               "gqa_last_error", "gqa_version"):
         assert n in names, n
@@ -161,3 +162,22 @@ def test_binding_rejects_host_tensors(lib):
     k = torch.zeros(1, 2, 16, 64)
     with pytest.raises(ValueError, match="GPU tensor"):
         gqa.decode(q, k, k, torch.zeros(1, dtype=torch.int32))
+
+
+def _append(lib, q=P, kn=P, vn=P, k=P, v=P, sl=P, out=P, B=2, H=8, G=2, d=64, n=128, scale=0.125,
+            dt=BF16, splits=0, ws=None, ws_bytes=0):
+    return lib.gqa_decode_append(q, kn, vn, k, v, sl, out, B, H, G, d, n, scale, dt, splits,
+                                 ws if ws is not None else ctypes.c_void_p(0), ws_bytes, None)
+
+
+def test_decode_append_rejects_bad_arguments(lib):
+    z = ctypes.c_void_p(0)
+    assert _append(lib, kn=z) == INVALID
+    assert _append(lib, vn=z) == INVALID
+    assert _append(lib, kn=P_MIS) == INVALID
+    assert "aligned" in lib.gqa_last_error().decode()
+    assert _append(lib, H=6, G=4) == INVALID
+    assert _append(lib, d=96) == UNSUPPORTED
+    assert _append(lib, B=16, H=32, G=8, d=128, n=1024) == WORKSPACE
+    # B = 0: nothing to do, no pointer looked at
+    assert _append(lib, q=z, kn=z, vn=z, k=z, v=z, sl=z, out=z, B=0) == OK
