@@ -99,15 +99,16 @@ def _time_calls(torch, fn, n_calls, warmup):
     return start.elapsed_time(end) / n_calls
 
 
-def bench_decode(torch, gqa, synth, name, G, steps, warmup, replicas_bytes=1 << 30):
+def bench_decode(torch, gqa, synth, name, G, steps, warmup, replicas_bytes=1 << 30, append=False):
     w = synth.WORKLOADS[name]
     B, H, d, N = w.B, w.H, w.d, w.N
     dev = "cuda:0"
     itemsize = 2 if w.dtype == "bf16" else 4
     kv_bytes = 2 * B * G * N * d * itemsize
     R = 1 if w.seqlens == "uniform" else max(1, min(64, math.ceil(replicas_bytes / kv_bytes)))
-    reps = [synth.decode_inputs(B, H, G, d, N, dtype=w.dtype, seed=w.seed + r, device=dev,
-                                seqlens=w.seqlens, nan_tail=w.nan_tail) for r in range(R)]
+    make = synth.decode_append_inputs if append else synth.decode_inputs
+    reps = [make(B, H, G, d, N, dtype=w.dtype, seed=w.seed + r, device=dev,
+                 seqlens=w.seqlens, nan_tail=w.nan_tail) for r in range(R)]
     q = reps[0]["q"]
     out = torch.empty_like(q)
     # zero-filled once; the library leaves its counter header zero after each call
@@ -116,14 +117,20 @@ def bench_decode(torch, gqa, synth, name, G, steps, warmup, replicas_bytes=1 << 
 
     def call(i):
         x = reps[i % R]
-        gqa.decode(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=scale, out=out,
-                   workspace=ws)
+        if append:      # the same row is written again on every call: idempotent
+            gqa.decode_append(x["q"], x["k_new"], x["v_new"], x["k_cache"], x["v_cache"],
+                              x["seqlens"], scale=scale, out=out, workspace=ws)
+        else:
+            gqa.decode(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=scale, out=out,
+                       workspace=ws)
 
     ms = _time_calls(torch, call, steps, warmup)
     total_pos = int(torch.clamp(reps[0]["seqlens"].long(), 0, N).sum().item())
     for r in reps[1:]:
         assert int(torch.clamp(r["seqlens"].long(), 0, N).sum().item()) == total_pos
     nbytes = decode_bytes(B, H, G, d, total_pos, itemsize)
+    if append:          # the new rows: read from k_new/v_new and written into the caches
+        nbytes += 2 * 2 * B * G * d * itemsize
     gbps = nbytes / (ms * 1e-3) / 1e9
     res = {
         "B": B, "H": H, "G": G, "d": d, "N": N, "dtype": w.dtype,
@@ -268,6 +275,8 @@ def main():
     if not args.quick:
         for g in (32, 4, 1):
             secondary[f"llama7b_decode_G{g}"] = bench_decode(torch, gqa, synth, name, g, args.steps, args.warmup)
+        secondary["llama7b_decode_append_G8"] = bench_decode(torch, gqa, synth, name, 8, args.steps,
+                                                              args.warmup, append=True)
         secondary["t5xxl_cross_decode"] = bench_decode(torch, gqa, synth, "t5xxl_cross_decode_bf16", 8,
                                                        args.steps, args.warmup)
         secondary["ragged_longctx_decode"] = bench_decode(torch, gqa, synth, "ragged_longctx_decode_bf16",
