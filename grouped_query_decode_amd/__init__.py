@@ -30,7 +30,7 @@ _LIB_NAME = "libgqa.so"
 _lib = None
 _workspaces: dict = {}
 
-DTYPE_CODES = {torch.float32: 0, torch.bfloat16: 1}
+DTYPE_CODES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
 
 class GQAError(RuntimeError):
@@ -95,7 +95,7 @@ def _dtype_code(t: torch.Tensor) -> int:
     try:
         return DTYPE_CODES[t.dtype]
     except KeyError:
-        raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)") from None
+        raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float16)") from None
 
 
 def _require_device(name: str, t: torch.Tensor, device) -> None:

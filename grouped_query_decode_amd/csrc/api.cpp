@@ -30,6 +30,10 @@ gqa_status fail(gqa_status s, const char* fmt, ...) {
 
 gqa_status ok() { return GQA_OK; }
 
+bool known_dtype(int dtype) {
+  return dtype == GQA_DTYPE_F32 || dtype == GQA_DTYPE_BF16 || dtype == GQA_DTYPE_F16;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -109,8 +113,7 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
                        const void* k_new = nullptr, const void* v_new = nullptr) {
   g_last_error.clear();
   const bool append = k_new != nullptr || v_new != nullptr;
-  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
-    return fail(GQA_ERR_INVALID_ARG, "gqa_decode: unknown dtype %d", dtype);
+  if (!known_dtype(dtype)) return fail(GQA_ERR_INVALID_ARG, "gqa_decode: unknown dtype %d", dtype);
   if (B < 0 || n_max < 0)
     return fail(GQA_ERR_INVALID_ARG, "gqa_decode: negative size (B=%d, n_max=%d)", B, n_max);
   if (B == 0) return ok();
@@ -155,7 +158,7 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
   const int n_rep = H / G;
 
-  if (dtype == GQA_DTYPE_BF16 && gqa::decode_mfma_supports(n_rep, d, S, split_len)) {
+  if (dtype != GQA_DTYPE_F32 && gqa::decode_mfma_supports(n_rep, d, S, split_len)) {
     gqa::DecodeProblem p{};
     p.q = static_cast<const uint16_t*>(q);
     p.k = static_cast<const uint16_t*>(k);
@@ -168,6 +171,7 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
     p.counters = (S > 1 && int64_t(B) * G <= kMaxCountedUnits) ? counters : nullptr;
     p.k_new = static_cast<const uint16_t*>(k_new);
     p.v_new = static_cast<const uint16_t*>(v_new);
+    p.dtype = dtype;
     p.B = B; p.H = H; p.G = G; p.n_rep = n_rep; p.d = d; p.n_max = n_max;
     p.scale = scale;
     p.num_splits = S;
@@ -260,7 +264,7 @@ gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new
 gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void* out, int B,
                               int T, int H, int G, int d, float scale, int dtype, void* stream_v) {
   g_last_error.clear();
-  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+  if (!known_dtype(dtype))
     return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: unknown dtype %d", dtype);
   if (B < 0 || T < 0)
     return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: negative size (B=%d, T=%d)", B, T);
@@ -281,7 +285,7 @@ gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void*
     return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: problem too large");
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
   const int n_rep = H / G;
-  if (dtype == GQA_DTYPE_BF16 && gqa::prefill_mfma_supports(n_rep, d)) {
+  if (dtype != GQA_DTYPE_F32 && gqa::prefill_mfma_supports(n_rep, d)) {
     gqa::PrefillProblem p{};
     p.q = static_cast<const uint16_t*>(q);
     p.k = static_cast<const uint16_t*>(k);
@@ -289,6 +293,7 @@ gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void*
     p.out = static_cast<uint16_t*>(out);
     p.B = B; p.T = T; p.H = H; p.G = G; p.n_rep = n_rep; p.d = d;
     p.scale = scale;
+    p.dtype = dtype;
     return launched(gqa::launch_prefill_mfma(p, stream), "gqa_prefill_causal");
   }
   gqa::RowsProblem p{};
@@ -310,7 +315,7 @@ gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void*
 gqa_status kv_meanpool_heads(const void* w_in, void* w_out, int H, int G, int64_t per_head_elems,
                              int dtype, void* stream_v) {
   g_last_error.clear();
-  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+  if (!known_dtype(dtype))
     return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: unknown dtype %d", dtype);
   if (H < 1 || G < 1 || H % G != 0)
     return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: H=%d must be a positive multiple of G=%d",

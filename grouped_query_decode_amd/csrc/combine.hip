@@ -40,6 +40,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineProblem p) {
     const int64_t oi = pair * p.d + col;
     if (DT == kF32)
       static_cast<float*>(p.out)[oi] = val;
+    else if (DT == kF16)
+      static_cast<uint16_t*>(p.out)[oi] = to_f16(val);
     else
       static_cast<uint16_t*>(p.out)[oi] = to_bf16(val);
   }
@@ -53,6 +55,8 @@ hipError_t launch_combine(const CombineProblem& p, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
   if (p.dtype == kF32)
     hipLaunchKernelGGL(combine_kernel<kF32>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  else if (p.dtype == kF16)
+    hipLaunchKernelGGL(combine_kernel<kF16>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL(combine_kernel<kBF16>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
   return hipGetLastError();

@@ -1,4 +1,5 @@
-// GQA decode step on the gfx950 matrix cores (bfloat16 in, float32 accumulate).
+// GQA decode step on the gfx950 matrix cores (bfloat16 or IEEE half in, float32
+// accumulate; below, "16-bit" is whichever of the two the call uses).
 //
 // Definition: fogdragon CSDN blog, section "KV Cache" (append, then
 // softmax(scale * q.K) over the cached positions and a weighted sum of V);
@@ -9,12 +10,12 @@
 // matrix-core tiles (padded with zero queries), so every cached K/V row is read
 // from HBM once and used by all heads of its group:
 //
-//   scores  S^T[key][head] = K[key][:] . Q[head][:]     16x16x32 bf16 MFMA,
+//   scores  S^T[key][head] = K[key][:] . Q[head][:]     16x16x32 16-bit MFMA,
 //           A = 16 keys x 32 dims straight from HBM (16-byte loads),
 //           B = the group's queries (registers, loaded once)
 //   softmax online, base 2 (hardware exp2), float32; the weights are rounded
-//           to bf16 and the normaliser sums the rounded weights (so constant V
-//           is exact)
+//           to the 16-bit format and the normaliser sums the rounded weights
+//           (so constant V is exact)
 //   output  O^T[dim][head] += V^T[dim][key] P^T[key][head]   16x16x32 MFMA,
 //           A = V^T read with transposing LDS loads from a per-wave copy of
 //           the 32-row V tile, B = the weights, already in the right lanes
@@ -63,8 +64,15 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(const_cast<char*>(p)));
 }
 
-__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// 16x16x32 MFMA on raw 16-bit operands: bfloat16 or IEEE half (DT).
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  if constexpr (DT == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
 // Partials cross workgroups (and XCDs, whose L2s are not coherent with each
@@ -101,9 +109,10 @@ struct UnitPartials {
 // and 8-column chunk c8 of sequence b, written to out.  Splits are read 8 at
 // a time with all their loads in flight together; the running maximum is
 // rescaled per batch.
-template <int D>
+template <int D, int DT>
 __device__ __forceinline__ void merge_item(const DecodeProblem& p, const UnitPartials<D>& up, int b, int ns,
                                            int h, int hl, int c8) {
+  using H16 = Half16<DT>;
   const int S = p.num_splits;
   float M = -INFINITY, L = 0.f;
   f32x4_t Oa = {0.f, 0.f, 0.f, 0.f}, Ob = {0.f, 0.f, 0.f, 0.f};
@@ -142,13 +151,14 @@ __device__ __forceinline__ void merge_item(const DecodeProblem& p, const UnitPar
   }
   const float inv = L > 0.f ? __builtin_amdgcn_rcpf(L) : 0.f;
   st16(p.out + (int64_t(b) * p.H + h) * D + c8 * 8,
-       u32x4_t{pack_bf16x2(Oa[0] * inv, Oa[1] * inv), pack_bf16x2(Oa[2] * inv, Oa[3] * inv),
-               pack_bf16x2(Ob[0] * inv, Ob[1] * inv), pack_bf16x2(Ob[2] * inv, Ob[3] * inv)});
+       u32x4_t{H16::pack2(Oa[0] * inv, Oa[1] * inv), H16::pack2(Oa[2] * inv, Oa[3] * inv),
+               H16::pack2(Ob[0] * inv, Ob[1] * inv), H16::pack2(Ob[2] * inv, Ob[3] * inv)});
 }
 
-template <int D, int NHB>
+template <int D, int NHB, int DT>
 __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(DecodeProblem p) {
   using C = Cfg<D>;
+  using H16 = Half16<DT>;
   __shared__ __attribute__((aligned(16))) char smem[C::kLds];
   __shared__ int s_last;
 
@@ -203,7 +213,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
 
   // Queries of the group: B operand of the score MFMA, lane = head lo of head
   // block hb, k-slot group hi covers dims 8*(4*ks + hi) .. +7.
-  bf16x8_t qop[NHB][C::kSteps];
+  u32x4_t qop[NHB][C::kSteps];
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     const int hl = hb * 16 + lo;
@@ -213,7 +223,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
     for (int ks = 0; ks < C::kSteps; ++ks) {
       u32x4_t w = {0u, 0u, 0u, 0u};
       if (hv) w = ld16(qrow + (4 * ks + hi) * 8);
-      qop[hb][ks] = __builtin_bit_cast(bf16x8_t, w);
+      qop[hb][ks] = w;
     }
   }
 
@@ -281,7 +291,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
         f32x4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < C::kSteps; ++ks)
-          a = mfma16(__builtin_bit_cast(bf16x8_t, kr[blk][ks]), qop[hb][ks], a);
+          a = mfma16<DT>(kr[blk][ks], qop[hb][ks], a);
         sacc[hb][blk] = a;
       }
     // this tile's registers are free: fetch the tile after next into them
@@ -289,7 +299,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
 
     // online softmax; lane holds keys 16*blk + 4*hi + r of the tile, head lo
     const int rel0 = tile * kKT + 4 * hi;
-    bf16x8_t pop[NHB];
+    u32x4_t pop[NHB];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       float t2[2][4];
@@ -313,13 +323,13 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r2 = 0; r2 < 2; ++r2) {
-          const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(t2[blk][2 * r2] - mn),
-                                          __builtin_amdgcn_exp2f(t2[blk][2 * r2 + 1] - mn));
+          const uint32_t pk = H16::pack2(__builtin_amdgcn_exp2f(t2[blk][2 * r2] - mn),
+                                         __builtin_amdgcn_exp2f(t2[blk][2 * r2 + 1] - mn));
           w[blk * 2 + r2] = pk;
-          lsum += bf16lo_to_f32(pk) + bf16hi_to_f32(pk);
+          lsum += H16::lo(pk) + H16::hi(pk);
         }
       lrun[hb] = fmaf(lrun[hb], alpha, lsum);
-      pop[hb] = __builtin_bit_cast(bf16x8_t, u32x4_t{w[0], w[1], w[2], w[3]});
+      pop[hb] = u32x4_t{w[0], w[1], w[2], w[3]};
 #pragma unroll
       for (int cb = 0; cb < C::kColBlocks; ++cb) acc[hb][cb] *= alpha;
     }
@@ -331,9 +341,9 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
     for (int cb = 0; cb < C::kColBlocks; ++cb) {
       const i16x4_t a4 = lds_read_tr16(vt + cb * 32);
       const i16x4_t b4 = lds_read_tr16(vt + 16 * C::kPitch + cb * 32);
-      const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, i16x8_t{a4[0], a4[1], a4[2], a4[3], b4[0], b4[1], b4[2], b4[3]});
+      const u32x4_t vop = __builtin_bit_cast(u32x4_t, i16x8_t{a4[0], a4[1], a4[2], a4[3], b4[0], b4[1], b4[2], b4[3]});
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) acc[hb][cb] = mfma16(vop, pop[hb], acc[hb][cb]);
+      for (int hb = 0; hb < NHB; ++hb) acc[hb][cb] = mfma16<DT>(vop, pop[hb], acc[hb][cb]);
     }
   };
 
@@ -428,7 +438,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
       if (ns == 1) {
         const float inv = L > 0.f ? __builtin_amdgcn_rcpf(L) : 0.f;
         *reinterpret_cast<uint2*>(p.out + (int64_t(b) * p.H + h) * D + c4 * 4) =
-            make_uint2(pack_bf16x2(O[0] * inv, O[1] * inv), pack_bf16x2(O[2] * inv, O[3] * inv));
+            make_uint2(H16::pack2(O[0] * inv, O[1] * inv), H16::pack2(O[2] * inv, O[3] * inv));
       } else {
         const int pr = (16 * hb + hl) * S + s;       // within the unit's partials
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, O), up.o, pr * (D * 4) + c4 * 16, 0,
@@ -458,10 +468,10 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   constexpr int kC8 = D / 8;
 #pragma unroll 1
   for (int t = threadIdx.x; t < p.n_rep * kC8; t += blockDim.x)
-    merge_item<D>(p, up, b, ns, g * p.n_rep + t / kC8, t / kC8, t % kC8);
+    merge_item<D, DT>(p, up, b, ns, g * p.n_rep + t / kC8, t / kC8, t % kC8);
 }
 
-template <int D, int NHB>
+template <int D, int NHB, int DT>
 hipError_t launch_t(const DecodeProblem& p, hipStream_t stream) {
   const int64_t blocks = int64_t(p.B) * p.G * p.num_splits;
   if (blocks <= 0) return hipSuccess;
@@ -469,7 +479,7 @@ hipError_t launch_t(const DecodeProblem& p, hipStream_t stream) {
   // one wave per 32-position tile of a split, at most four
   const int tiles = (p.split_len + kKT - 1) / kKT;
   const int waves = tiles >= 4 ? 4 : (tiles >= 2 ? 2 : 1);
-  hipLaunchKernelGGL((decode_mfma_kernel<D, NHB>), dim3(unsigned(blocks)), dim3(64 * waves), 0,
+  hipLaunchKernelGGL((decode_mfma_kernel<D, NHB, DT>), dim3(unsigned(blocks)), dim3(64 * waves), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -486,11 +496,15 @@ bool decode_mfma_supports(int n_rep, int d, int num_splits, int split_len) {
          partials < (int64_t(1) << 31);
 }
 
+template <int DT>
+hipError_t launch_dt(const DecodeProblem& p, hipStream_t stream) {
+  if (p.d == 128)
+    return p.n_rep <= 16 ? launch_t<128, 1, DT>(p, stream) : launch_t<128, 2, DT>(p, stream);
+  return p.n_rep <= 16 ? launch_t<64, 1, DT>(p, stream) : launch_t<64, 2, DT>(p, stream);
+}
+
 hipError_t launch_decode_mfma(const DecodeProblem& p, hipStream_t stream) {
-  if (p.d == 128) {
-    return p.n_rep <= 16 ? launch_t<128, 1>(p, stream) : launch_t<128, 2>(p, stream);
-  }
-  return p.n_rep <= 16 ? launch_t<64, 1>(p, stream) : launch_t<64, 2>(p, stream);
+  return p.dtype == kF16 ? launch_dt<kF16>(p, stream) : launch_dt<kBF16>(p, stream);
 }
 
 }  // namespace gqa

@@ -8,6 +8,8 @@ namespace gqa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -30,6 +32,51 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ uint16_t to_bf16(float x) {
   return uint16_t(pack_bf16x2(x, 0.f) & 0xffffu);
 }
+
+// IEEE half: two floats -> two halves (round to nearest even), and back.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f32x2_t f = {lo, hi};
+  f16x2_t r = __builtin_convertvector(f, f16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ float f16lo_to_f32(uint32_t w) {
+  return float(__builtin_bit_cast(f16x2_t, w)[0]);
+}
+__device__ __forceinline__ float f16hi_to_f32(uint32_t w) {
+  return float(__builtin_bit_cast(f16x2_t, w)[1]);
+}
+__device__ __forceinline__ uint16_t to_f16(float x) {
+  return uint16_t(pack_f16x2(x, 0.f) & 0xffffu);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return float(__builtin_bit_cast(_Float16, h));
+}
+
+// The two 16-bit element formats of the matrix-core paths, selected by the
+// dtype code (1 = bfloat16, 2 = IEEE half): packing of float pairs (round to
+// nearest even), unpacking, and the sum of a packed pair in float32.
+template <int DT>
+struct Half16;
+template <>
+struct Half16<1> {
+  __device__ static uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+  __device__ static float lo(uint32_t w) { return bf16lo_to_f32(w); }
+  __device__ static float hi(uint32_t w) { return bf16hi_to_f32(w); }
+  __device__ static float sum2(uint32_t w, float acc) {   // acc + lo + hi (one dot2)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                           __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+  }
+};
+template <>
+struct Half16<2> {
+  __device__ static uint32_t pack2(float lo, float hi) { return pack_f16x2(lo, hi); }
+  __device__ static float lo(uint32_t w) { return f16lo_to_f32(w); }
+  __device__ static float hi(uint32_t w) { return f16hi_to_f32(w); }
+  __device__ static float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), __builtin_bit_cast(f16x2_t, 0x3c003c00u),
+                                  acc, false);
+  }
+};
 
 // 16-byte global load / store.
 __device__ __forceinline__ u32x4_t ld16(const void* p) {

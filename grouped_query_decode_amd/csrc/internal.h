@@ -6,7 +6,7 @@
 
 namespace gqa {
 
-enum Dtype { kF32 = 0, kBF16 = 1 };
+enum Dtype { kF32 = 0, kBF16 = 1, kF16 = 2 };
 
 // Generic "rows of queries attend a K/V head" problem, used by the vector-unit
 // kernel for decode (one row per sequence) and for float32 causal prefill (one
@@ -45,6 +45,7 @@ struct DecodeProblem {
   int* counters;            // [B*G] split-arrival counters (zero between calls), or null
   const uint16_t* k_new;    // [B, G, d] this step's k, v to append at seqlens[b]-1, or null
   const uint16_t* v_new;
+  int dtype;                // kBF16 or kF16
   int B, H, G, n_rep, d, n_max;
   float scale;
   int num_splits, split_len;
@@ -63,6 +64,7 @@ struct PrefillProblem {
   const uint16_t* k;        // [B, T, G, d]
   const uint16_t* v;
   uint16_t* out;            // [B, T, H, d]
+  int dtype;                // kBF16 or kF16
   int B, T, H, G, n_rep, d;
   float scale;
 };

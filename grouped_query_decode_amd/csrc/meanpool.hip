@@ -29,12 +29,12 @@ __global__ __launch_bounds__(256) void meanpool_vec8_kernel(MeanpoolProblem p) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int k = 0; k < p.n_rep; ++k) {
       const int64_t elem = (g * p.n_rep + k) * p.per_head_elems + e8 * 8;
-      if (DT == kBF16) {
+      if constexpr (DT != kF32) {
         const u32x4_t w = ld16(static_cast<const uint16_t*>(p.w_in) + elem);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          acc[2 * t] += bf16lo_to_f32(w[t]);
-          acc[2 * t + 1] += bf16hi_to_f32(w[t]);
+          acc[2 * t] += Half16<DT>::lo(w[t]);
+          acc[2 * t + 1] += Half16<DT>::hi(w[t]);
         }
       } else {
         const float* src = static_cast<const float*>(p.w_in) + elem;
@@ -48,10 +48,10 @@ __global__ __launch_bounds__(256) void meanpool_vec8_kernel(MeanpoolProblem p) {
       }
     }
     const int64_t oel = g * p.per_head_elems + e8 * 8;
-    if (DT == kBF16) {
+    if constexpr (DT != kF32) {
       u32x4_t w;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(acc[2 * t] / inv_div, acc[2 * t + 1] / inv_div);
+      for (int t = 0; t < 4; ++t) w[t] = Half16<DT>::pack2(acc[2 * t] / inv_div, acc[2 * t + 1] / inv_div);
       st16(static_cast<uint16_t*>(p.w_out) + oel, w);
     } else {
       u32x4_t a, b;
@@ -77,14 +77,16 @@ __global__ __launch_bounds__(256) void meanpool_scalar_kernel(MeanpoolProblem p)
     float acc = 0.f;
     for (int k = 0; k < p.n_rep; ++k) {
       const int64_t elem = (g * p.n_rep + k) * p.per_head_elems + e;
-      acc += DT == kBF16 ? bf16_to_f32(static_cast<const uint16_t*>(p.w_in)[elem])
-                         : static_cast<const float*>(p.w_in)[elem];
+      if constexpr (DT == kF32)
+        acc += static_cast<const float*>(p.w_in)[elem];
+      else
+        acc += Half16<DT>::lo(static_cast<const uint16_t*>(p.w_in)[elem]);
     }
     const float mean = acc / float(p.n_rep);
-    if (DT == kBF16)
-      static_cast<uint16_t*>(p.w_out)[i] = to_bf16(mean);
-    else
+    if constexpr (DT == kF32)
       static_cast<float*>(p.w_out)[i] = mean;
+    else
+      static_cast<uint16_t*>(p.w_out)[i] = uint16_t(Half16<DT>::pack2(mean, 0.f) & 0xffffu);
   }
 }
 
@@ -97,16 +99,21 @@ hipError_t launch_meanpool(const MeanpoolProblem& p, hipStream_t stream) {
   int64_t blocks = (work + 255) / 256;
   if (blocks > 256 * 64) blocks = 256 * 64;
   if (blocks < 1) blocks = 1;
+  const dim3 grid = dim3(unsigned(blocks)), block = dim3(256);
   if (vec) {
     if (p.dtype == kBF16)
-      hipLaunchKernelGGL(meanpool_vec8_kernel<kBF16>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL(meanpool_vec8_kernel<kBF16>, grid, block, 0, stream, p);
+    else if (p.dtype == kF16)
+      hipLaunchKernelGGL(meanpool_vec8_kernel<kF16>, grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL(meanpool_vec8_kernel<kF32>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL(meanpool_vec8_kernel<kF32>, grid, block, 0, stream, p);
   } else {
     if (p.dtype == kBF16)
-      hipLaunchKernelGGL(meanpool_scalar_kernel<kBF16>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL(meanpool_scalar_kernel<kBF16>, grid, block, 0, stream, p);
+    else if (p.dtype == kF16)
+      hipLaunchKernelGGL(meanpool_scalar_kernel<kF16>, grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL(meanpool_scalar_kernel<kF32>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL(meanpool_scalar_kernel<kF32>, grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -1,4 +1,5 @@
-// Causal GQA prefill on the gfx950 matrix cores (bfloat16 in, float32 accumulate).
+// Causal GQA prefill on the gfx950 matrix cores (bfloat16 or IEEE half in,
+// float32 accumulate; "16-bit" below is whichever of the two the call uses).
 //
 // Definition: query position i of head h attends keys 0..i of K/V head
 // floor(h*G/H) through softmax(scale * q.k) and a weighted sum of v (fogdragon
@@ -11,13 +12,13 @@
 // heads x 4 blocks (n_rep = 2), or 1 head x 8 blocks (n_rep = 1), so every
 // K/V tile staged in LDS is used by 256 query rows.  Per 64-key tile and wave:
 //
-//   S^T[key][row] = K[key][:] . Q[row][:]        32x32x16 bf16 MFMA (2 x 8),
+//   S^T[key][row] = K[key][:] . Q[row][:]        32x32x16 16-bit MFMA (2 x 8),
 //                   A = K tile from LDS, B = the wave's queries (registers)
 //   mask j > i on tiles that reach the diagonal; online softmax in base 2,
 //   float32, one query row per lane column (max/sum in-lane plus one exchange)
 //   O^T[dim][row] += V^T[dim][key] P^T[key][row] 32x32x16 MFMA (4 x 4),
 //                   A = V^T from LDS (transposed once per workgroup when the
-//                   tile is staged), B = the bf16 weights, already in place
+//                   tile is staged), B = the 16-bit weights, already in place
 //
 // K/V tiles are double-buffered in LDS (layouts below): the next tiles'
 // global loads are issued before the current tile's math and land in the freed
@@ -25,8 +26,8 @@
 // deferred by one iteration so that each iteration hands the matrix unit and
 // the vector unit independent work.  Softmax work per score: one FMA
 // (scale folded in), one hardware exp2 (weights below 2^-126 may flush to
-// zero), a third of a max3, half a bf16 pack, half a
-// bf16 dot2 for the normaliser (which sums the rounded weights); the running
+// zero), a third of a max3, half a 16-bit pack, half a
+// 16-bit dot2 for the normaliser (which sums the rounded weights); the running
 // output is rescaled only when some row's maximum grew.  Query tiles are issued
 // heaviest first, and the query tiles of a (b, g) stay on one XCD (consecutive
 // workgroups go to consecutive XCDs) so its K/V stays in that XCD's L2.
@@ -63,8 +64,15 @@ struct PCfg {
   static constexpr int kBufBytes = kKBytes + kVBytes;
 };
 
-__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// 32x32x16 MFMA on raw 16-bit operands: bfloat16 or IEEE half (DT).
+template <int DT>
+__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+  if constexpr (DT == kBF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
 // Position of key kl (0..63) inside a V^T row: kl = 16u + 8a + 4h + b is
@@ -74,9 +82,10 @@ __device__ __forceinline__ int vt_pos(int kl) {
   return (kl & ~15) | ((kl & 4) << 1) | ((kl & 8) >> 1) | (kl & 3);
 }
 
-template <int D, int NW>
+template <int D, int NW, int DT>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillProblem p) {
   using C = PCfg<D>;
+  using H16 = Half16<DT>;
   constexpr int kThreads = 64 * NW;
   constexpr int kLoads = kKT * C::kChunks / kThreads;     // per thread per tile (K and V each)
   __shared__ __attribute__((aligned(16))) char smem[2 * C::kBufBytes];   // K0 K1 V0 V1
@@ -122,7 +131,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   // (a zero scale is replaced by a tiny one: the weights are then exactly
   // uniform, and masked scores still map to exactly zero weight)
   const float c2 = p.scale == 0.f ? 1e-30f : fabsf(p.scale) * kLog2e;
-  bf16x8_t qop[C::kSteps];
+  u32x4_t qop[C::kSteps];
   {
     const bool rv = t_row < p.T;
     const uint16_t* qrow = p.q + ((int64_t(b) * p.T + (rv ? t_row : 0)) * p.H + head) * D;
@@ -131,7 +140,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
       u32x4_t w = {0u, 0u, 0u, 0u};
       if (rv) w = ld16(qrow + 16 * ks + 8 * h2);
       w ^= u32x4_t{qsign, qsign, qsign, qsign};
-      qop[ks] = __builtin_bit_cast(bf16x8_t, w);
+      qop[ks] = w;
     }
   }
 
@@ -230,16 +239,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
     for (int ks = 0; ks < C::kSteps; ++ks) {
       const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(krow0 + ks * 32);
       const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(krow0 + 32 * C::kKPitch + ks * 32);
-      sc[0] = mfma32(__builtin_bit_cast(bf16x8_t, k0), qop[ks], sc[0]);
-      sc[1] = mfma32(__builtin_bit_cast(bf16x8_t, k1), qop[ks], sc[1]);
+      sc[0] = mfma32<DT>(k0, qop[ks], sc[0]);
+      sc[1] = mfma32<DT>(k1, qop[ks], sc[1]);
     }
   };
 
-  // Online softmax of one tile's scores (masked near the diagonal): bf16
+  // Online softmax of one tile's scores (masked near the diagonal): 16-bit
   // weights as PV B operands (one per 16-key step u: keys 16u + 8*(e/4) +
   // 4*h2 + e%4), the new running maximum, and the factor the running output
   // must be scaled by before these weights are added to it.
-  auto softmax = [&](f32x16_t* sc, int key0, bool masked, bf16x8_t* pop, float& alpha, bool& rescale) {
+  auto softmax = [&](f32x16_t* sc, int key0, bool masked, u32x4_t* pop, float& alpha, bool& rescale) {
     if (masked) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -265,11 +274,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
         const int r0 = 8 * (u & 1) + 2 * e2;
         const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[u >> 1][r0], c2, -mc));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[u >> 1][r0 + 1], c2, -mc));
-        w[e2] = pack_bf16x2(p0, p1);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e2]),
-                                               __builtin_bit_cast(bf16x2_t, 0x3f803f80u), lsum, false);
+        w[e2] = H16::pack2(p0, p1);
+        lsum = H16::sum2(w[e2], lsum);
       }
-      pop[u] = __builtin_bit_cast(bf16x8_t, u32x4_t{w[0], w[1], w[2], w[3]});
+      pop[u] = u32x4_t{w[0], w[1], w[2], w[3]};
     }
     alpha = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun * c2 - mc);
     rescale = __any(mn != mrun);                   // some row's maximum grew
@@ -280,16 +288,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   // O^T += V^T P^T: A = V^T[32*cb + l32][keys of k-step u, half h2], one
   // 16-byte read (keys stored contiguously, see vt_pos)
   const int vt_lane = l32 * C::kVtPitch + h2 * 16;
-  auto pv = [&](const bf16x8_t* pop, const char* sv) {
+  auto pv = [&](const u32x4_t* pop, const char* sv) {
     const char* vlane = sv + vt_lane;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      bf16x8_t vop[C::kColBlocks];
+      u32x4_t vop[C::kColBlocks];
 #pragma unroll
       for (int cb = 0; cb < C::kColBlocks; ++cb)
-        vop[cb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(vlane + (32 * cb) * C::kVtPitch + 32 * u));
+        vop[cb] = *reinterpret_cast<const u32x4_t*>(vlane + (32 * cb) * C::kVtPitch + 32 * u);
 #pragma unroll
-      for (int cb = 0; cb < C::kColBlocks; ++cb) acc[cb] = mfma32(vop[cb], pop[u], acc[cb]);
+      for (int cb = 0; cb < C::kColBlocks; ++cb) acc[cb] = mfma32<DT>(vop[cb], pop[u], acc[cb]);
     }
   };
   auto rescale_acc = [&](float alpha) {
@@ -317,7 +325,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   __syncthreads();
   f32x16_t scur[2], snext[2];
   qk(kslot(0), scur);
-  bf16x8_t pprev[4];
+  u32x4_t pprev[4];
   float alpha_prev = 1.f;
   bool rescale_prev = false;
 
@@ -372,8 +380,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int col = 32 * cb + 8 * r4 + 4 * h2;
-        const uint32_t w0 = pack_bf16x2(acc[cb][4 * r4] * inv, acc[cb][4 * r4 + 1] * inv);
-        const uint32_t w1 = pack_bf16x2(acc[cb][4 * r4 + 2] * inv, acc[cb][4 * r4 + 3] * inv);
+        const uint32_t w0 = H16::pack2(acc[cb][4 * r4] * inv, acc[cb][4 * r4 + 1] * inv);
+        const uint32_t w1 = H16::pack2(acc[cb][4 * r4 + 2] * inv, acc[cb][4 * r4 + 3] * inv);
         *reinterpret_cast<uint2*>(orow + col) = make_uint2(w0, w1);
       }
   }
@@ -393,10 +401,18 @@ hipError_t launch_prefill_mfma(const PrefillProblem& p, hipStream_t stream) {
   const int64_t blocks = n_qt * p.B * p.G * (p.n_rep / nre);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (p.d == 128)
-    hipLaunchKernelGGL((prefill_mfma_kernel<128, NW>), dim3(unsigned(blocks)), dim3(64 * NW), 0, stream, p);
-  else
-    hipLaunchKernelGGL((prefill_mfma_kernel<64, NW>), dim3(unsigned(blocks)), dim3(64 * NW), 0, stream, p);
+  const dim3 grid = dim3(unsigned(blocks)), block = dim3(64 * NW);
+  if (p.dtype == kF16) {
+    if (p.d == 128)
+      hipLaunchKernelGGL((prefill_mfma_kernel<128, NW, kF16>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((prefill_mfma_kernel<64, NW, kF16>), grid, block, 0, stream, p);
+  } else {
+    if (p.d == 128)
+      hipLaunchKernelGGL((prefill_mfma_kernel<128, NW, kBF16>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((prefill_mfma_kernel<64, NW, kBF16>), grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 

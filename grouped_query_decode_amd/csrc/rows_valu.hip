@@ -50,6 +50,22 @@ struct Elem<kBF16> {
   }
 };
 
+template <>
+struct Elem<kF16> {
+  static constexpr int kSize = 2;
+  __device__ static void load16(const char* p, float* f) {
+    u32x4_t w = ld16(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = f16lo_to_f32(w[i]);
+      f[2 * i + 1] = f16hi_to_f32(w[i]);
+    }
+  }
+  __device__ static void store(char* p, int i, float x) {
+    reinterpret_cast<uint16_t*>(p)[i] = to_f16(x);
+  }
+};
+
 template <int DT, int D>
 __global__ __launch_bounds__(256) void rows_valu_kernel(RowsProblem p) {
   using E = Elem<DT>;
@@ -227,6 +243,9 @@ hipError_t launch_t(const RowsProblem& p, hipStream_t stream) {
 hipError_t launch_rows_valu(const RowsProblem& p, int dtype, hipStream_t stream) {
   if (dtype == kF32) {
     return p.d == 64 ? launch_t<kF32, 64>(p, stream) : launch_t<kF32, 128>(p, stream);
+  }
+  if (dtype == kF16) {
+    return p.d == 64 ? launch_t<kF16, 64>(p, stream) : launch_t<kF16, 128>(p, stream);
   }
   return p.d == 64 ? launch_t<kBF16, 64>(p, stream) : launch_t<kBF16, 128>(p, stream);
 }

@@ -14,9 +14,11 @@
  * - Tensor arguments are DEVICE pointers owned by the caller, dense and
  *   row-major in the shapes given below, each 16-byte aligned.  The library
  *   never allocates, frees or keeps them after the call returns.
- * - dtype is GQA_DTYPE_F32 (float) or GQA_DTYPE_BF16 (bfloat16); inputs and
- *   outputs share it.  Arithmetic is float32 throughout; a bfloat16 output is
- *   rounded once, to nearest even.
+ * - dtype is GQA_DTYPE_F32 (float), GQA_DTYPE_BF16 (bfloat16) or GQA_DTYPE_F16
+ *   (IEEE half); inputs and outputs share it.  Arithmetic is float32
+ *   throughout; a 16-bit output is rounded once, to nearest even.  On the
+ *   16-bit paths the attention weights are rounded to the same 16-bit format
+ *   before they multiply V (the matrix cores take 16-bit operands).
  * - stream is a hipStream_t passed as void* (NULL: the null stream).  Work is
  *   enqueued asynchronously on it; the library never synchronises.  A fault
  *   inside a kernel surfaces at the caller's next synchronisation.
@@ -40,7 +42,8 @@ extern "C" {
 
 enum {
   GQA_DTYPE_F32 = 0,
-  GQA_DTYPE_BF16 = 1
+  GQA_DTYPE_BF16 = 1,
+  GQA_DTYPE_F16 = 2
 };
 
 typedef enum gqa_status {
@@ -134,7 +137,7 @@ gqa_status gqa_decode_split(const void* q, const void* k_cache, const void* v_ca
 
 /*
  * gqa_decode_append - append this step's k, v to the caches, then decode, in
- * one call (one kernel launch on the bfloat16 path).
+ * one call (one kernel launch on the 16-bit paths).
  *
  * Defines (the fogdragon CSDN blog, section "KV Cache": each step
  * concatenates its new k and v onto the cached K and V -- K = cat(K_prev, k),
@@ -179,10 +182,10 @@ gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new
  *   out  [B, T, H, d]   dtype, device; written in full.
  *   d    64 or 128.
  *
- * bfloat16 runs on the matrix cores (bf16 products, float32 accumulation; the
- * softmax weights are rounded to bf16 before they multiply V, and the
- * normaliser sums those rounded weights).  float32 runs on the vector units
- * in float32.  Errors as for gqa_decode; B = 0 or T = 0 is a valid no-op.
+ * bfloat16 and IEEE half run on the matrix cores (16-bit products, float32
+ * accumulation; the softmax weights are rounded to the 16-bit format before
+ * they multiply V, and the normaliser sums those rounded weights).  float32
+ * runs on the vector units in float32.  Errors as for gqa_decode; B = 0 or T = 0 is a valid no-op.
  */
 gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void* out,
                               int B, int T, int H, int G, int d, float scale, int dtype,

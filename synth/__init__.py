@@ -38,7 +38,7 @@ __all__ = [
 
 
 def torch_dtype(name: str) -> torch.dtype:
-    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[name]
 
 
 def scale_for(d: int) -> float:

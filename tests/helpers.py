@@ -10,6 +10,10 @@ import torch
 F32_MAX_ABS = 1e-5
 BF16_MAX_ABS = 1.5e-2
 BF16_MEAN_ABS = 2e-3
+# IEEE half keeps 3 more mantissa bits than bfloat16 (the attention weights
+# and the output are rounded to it): the bfloat16 bounds divided by 4.
+F16_MAX_ABS = 4e-3
+F16_MEAN_ABS = 5e-4
 
 
 def need_gpu():
@@ -35,6 +39,8 @@ def assert_close(got: torch.Tensor, ref: np.ndarray, dtype: torch.dtype, what: s
     stats = {"max_abs": float(err.max(initial=0.0)), "mean_abs": float(err.mean()) if err.size else 0.0}
     if dtype == torch.float32:
         assert stats["max_abs"] <= F32_MAX_ABS, f"{what}: {stats}"
+    elif dtype == torch.float16:
+        assert stats["max_abs"] <= F16_MAX_ABS and stats["mean_abs"] <= F16_MEAN_ABS, f"{what}: {stats}"
     else:
         assert stats["max_abs"] <= BF16_MAX_ABS and stats["mean_abs"] <= BF16_MEAN_ABS, f"{what}: {stats}"
     return stats
@@ -46,6 +52,16 @@ def bf16_ulp_distance(got_bf16: torch.Tensor, ref: np.ndarray) -> np.ndarray:
     a = got_bf16.detach().cpu().view(torch.int16).numpy().astype(np.int64)
     b = want.view(torch.int16).numpy().astype(np.int64)
     # map sign-magnitude to a monotone integer line
+    a = np.where(a < 0, -(a & 0x7FFF), a)
+    b = np.where(b < 0, -(b & 0x7FFF), b)
+    return np.abs(a - b)
+
+
+def f16_ulp_distance(got_f16: torch.Tensor, ref: np.ndarray) -> np.ndarray:
+    """|bits(got) - bits(RNE_f16(ref))| as integers (same-sign values assumed near)."""
+    want = torch.from_numpy(ref.astype(np.float32)).to(torch.float16)
+    a = got_f16.detach().cpu().view(torch.int16).numpy().astype(np.int64)
+    b = want.view(torch.int16).numpy().astype(np.int64)
     a = np.where(a < 0, -(a & 0x7FFF), a)
     b = np.where(b < 0, -(b & 0x7FFF), b)
     return np.abs(a - b)
