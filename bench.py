@@ -99,15 +99,17 @@ def _time_calls(torch, fn, n_calls, warmup):
     return start.elapsed_time(end) / n_calls
 
 
-def bench_decode(torch, gqa, synth, name, G, steps, warmup, replicas_bytes=1 << 30, append=False):
+def bench_decode(torch, gqa, synth, name, G, steps, warmup, replicas_bytes=1 << 30, append=False,
+                 dtype=None):
     w = synth.WORKLOADS[name]
     B, H, d, N = w.B, w.H, w.d, w.N
+    dt = dtype or w.dtype
     dev = "cuda:0"
-    itemsize = 2 if w.dtype == "bf16" else 4
+    itemsize = 4 if dt == "f32" else 2
     kv_bytes = 2 * B * G * N * d * itemsize
     R = 1 if w.seqlens == "uniform" else max(1, min(64, math.ceil(replicas_bytes / kv_bytes)))
     make = synth.decode_append_inputs if append else synth.decode_inputs
-    reps = [make(B, H, G, d, N, dtype=w.dtype, seed=w.seed + r, device=dev,
+    reps = [make(B, H, G, d, N, dtype=dt, seed=w.seed + r, device=dev,
                  seqlens=w.seqlens, nan_tail=w.nan_tail) for r in range(R)]
     q = reps[0]["q"]
     out = torch.empty_like(q)
@@ -133,7 +135,7 @@ def bench_decode(torch, gqa, synth, name, G, steps, warmup, replicas_bytes=1 << 
         nbytes += 2 * 2 * B * G * d * itemsize
     gbps = nbytes / (ms * 1e-3) / 1e9
     res = {
-        "B": B, "H": H, "G": G, "d": d, "N": N, "dtype": w.dtype,
+        "B": B, "H": H, "G": G, "d": d, "N": N, "dtype": dt,
         "splits": gqa.decode_num_splits(B, H, G, d, N), "replicas": R,
         "ms_per_call": round(ms, 6), "bytes_per_call": nbytes,
         "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
@@ -145,9 +147,10 @@ def bench_decode(torch, gqa, synth, name, G, steps, warmup, replicas_bytes=1 << 
     return res
 
 
-def bench_prefill(torch, gqa, synth, steps, warmup):
+def bench_prefill(torch, gqa, synth, steps, warmup, dtype=None):
     w = synth.WORKLOADS["causal_prefill_bf16"]
-    x = synth.prefill_inputs(w.B, w.N, w.H, w.G, w.d, dtype=w.dtype, seed=w.seed,
+    dt = dtype or w.dtype
+    x = synth.prefill_inputs(w.B, w.N, w.H, w.G, w.d, dtype=dt, seed=w.seed,
                              device="cuda:0", std=w.std)
     out = torch.empty_like(x["q"])
     scale = synth.scale_for(w.d)
@@ -157,7 +160,7 @@ def bench_prefill(torch, gqa, synth, steps, warmup):
     tf = fl / (ms * 1e-3) / 1e12
     del x, out
     torch.cuda.empty_cache()
-    return {"B": w.B, "T": w.N, "H": w.H, "G": w.G, "d": w.d, "dtype": w.dtype,
+    return {"B": w.B, "T": w.N, "H": w.H, "G": w.G, "d": w.d, "dtype": dt,
             "ms_per_call": round(ms, 6), "flops_per_call": fl, "TFLOPs": round(tf, 1),
             "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
             "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1)}
@@ -281,7 +284,11 @@ def main():
                                                        args.steps, args.warmup)
         secondary["ragged_longctx_decode"] = bench_decode(torch, gqa, synth, "ragged_longctx_decode_bf16",
                                                           8, max(20, args.steps // 5), 3)
+        secondary["llama7b_decode_G8_f16"] = bench_decode(torch, gqa, synth, name, 8, args.steps,
+                                                           args.warmup, dtype="f16")
         secondary["causal_prefill"] = bench_prefill(torch, gqa, synth, max(20, args.steps // 5), 3)
+        secondary["causal_prefill_f16"] = bench_prefill(torch, gqa, synth, max(20, args.steps // 5), 3,
+                                                        dtype="f16")
         secondary["t5xxl_meanpool"] = bench_meanpool(torch, gqa, synth, args.steps, args.warmup)
         secondary["hbm_copy_probe"] = bench_copy_probe(torch, args.steps)
         secondary["hbm_read_probe"] = bench_read_probe(torch, args.steps)
