@@ -18,6 +18,11 @@ from .gqa_oracle import (  # noqa: F401
     decode_append_ref,
     future_keys,
     prefill_causal_ref,
+    chunk_attended_length,
+    prefill_chunk_ref,
+    gqkva_head_pair,
+    gqkva_decode_ref,
+    gqkva_prefill_causal_ref,
     meanpool_ref,
     kv_cache_values_per_token,
     kv_cache_bytes,

@@ -41,6 +41,17 @@ Readings taken where the pages are silent (each is also listed in the design doc):
   0 .. seqlens[b]-1.  A length of 0 has no position for the token and a length
   above Nmax points past the cache: in both cases nothing is written (the
   attention itself then follows the decode rules above).
+* Chunked prefill against a cache: a chunk of Tc new positions follows ctx
+  cached ones (its own k, v already in the cache at ctx .. ctx+Tc-1, as for
+  decode); chunk row t sits at absolute position ctx + t and attends positions
+  0 .. ctx + t inclusive -- the causal rule of the prompt phase with an offset
+  (Tc = 1 is the decode step, ctx = 0 the whole-prompt prefill).  Positions
+  beyond the cache capacity Nmax are not attended (clamped); ctx < 0 reads as 0.
+* GQKVA (the GQKVA summary on hub.baai.ac.cn): g_q query projections and g_kv
+  key/value projections, attention for every (query group i, K/V group j)
+  pair, g_q * g_kv outputs.  The pages do not fix the order of the outputs;
+  here output head h pairs query group h // g_kv with K/V group h % g_kv
+  (query-group-major).
 * Mean-pooling is the arithmetic mean of the group's member heads.
 
 Pins: every function here is checked against something other than itself
@@ -63,6 +74,11 @@ __all__ = [
     "decode_append_ref",
     "future_keys",
     "prefill_causal_ref",
+    "chunk_attended_length",
+    "prefill_chunk_ref",
+    "gqkva_head_pair",
+    "gqkva_decode_ref",
+    "gqkva_prefill_causal_ref",
     "meanpool_ref",
     "kv_cache_values_per_token",
     "kv_cache_bytes",
@@ -258,6 +274,109 @@ def prefill_causal_ref(q, k, v, scale: float, rows=None) -> np.ndarray:
             scores = float(scale) * logits
             scores = np.where(future, -np.inf, scores)
             out[b, rows, h, :] = softmax_weights(scores) @ Vbg
+    return out
+
+
+def chunk_attended_length(ctx: int, t: int, n_max: int) -> int:
+    """Positions attended by row t of a chunk that follows ``ctx`` cached positions.
+
+    The prompt phase's causal rule (a position sees itself and everything
+    before it) with the chunk offset: absolute position ctx + t attends
+    ctx + t + 1 positions, at most the ``n_max`` that exist.
+    """
+    ctx = max(int(ctx), 0)
+    return int(min(ctx + int(t) + 1, int(n_max)))
+
+
+def prefill_chunk_ref(q, k_cache, v_cache, ctx_lens, scale: float, rows=None) -> np.ndarray:
+    """A prompt chunk attending the cache it extends, in float64.  Returns out[B, Tc, H, d].
+
+    q: [B, Tc, H, d]; k_cache, v_cache: [B, G, Nmax, d] holding the ctx_lens[b]
+    earlier positions and the chunk's own positions after them; ctx_lens: [B].
+    Row t of sequence b, head h, attends the first
+    ``chunk_attended_length(ctx_lens[b], t, Nmax)`` positions of K/V head
+    ``kv_group_of_head(h, H, G)`` with ``attend_one_query``.  ``rows``
+    (optional) restricts the computation to those chunk rows; the other output
+    rows are NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_cache = np.asarray(k_cache, dtype=np.float64)
+    v_cache = np.asarray(v_cache, dtype=np.float64)
+    ctx_lens = np.asarray(ctx_lens).reshape(-1)
+    B, Tc, H, d = q.shape
+    Bk, G, n_max, dk = k_cache.shape
+    if (Bk, dk) != (B, d) or v_cache.shape != k_cache.shape or ctx_lens.shape[0] != B:
+        raise ValueError("inconsistent chunk shapes")
+    rows = range(Tc) if rows is None else [int(r) for r in np.asarray(rows).reshape(-1)]
+    out = np.full((B, Tc, H, d), np.nan, dtype=np.float64)
+    for b in range(B):
+        for t in rows:
+            n = chunk_attended_length(ctx_lens[b], t, n_max)
+            for h in range(H):
+                g = kv_group_of_head(h, H, G)
+                if n == 0:
+                    out[b, t, h] = 0.0
+                    continue
+                out[b, t, h] = attend_one_query(q[b, t, h], k_cache[b, g, :n], v_cache[b, g, :n], scale)
+    return out
+
+
+def gqkva_head_pair(h: int, g_q: int, g_kv: int) -> tuple[int, int]:
+    """(query group, K/V group) of output head h under GQKVA (query-group-major)."""
+    if g_q < 1 or g_kv < 1 or not 0 <= h < g_q * g_kv:
+        raise ValueError("bad GQKVA head")
+    return h // g_kv, h % g_kv
+
+
+def gqkva_decode_ref(q, k_cache, v_cache, seqlens, scale: float) -> np.ndarray:
+    """One GQKVA decode step, in float64.  Returns out[B, g_q * g_kv, d].
+
+    q: [B, g_q, d] (one query per query group); k_cache, v_cache:
+    [B, g_kv, Nmax, d].  Output head h = (i, j) = ``gqkva_head_pair`` attends
+    the first ``attended_length`` cached positions of K/V group j with query
+    group i's query (GQKVA summary: attention over every (Q, KV) combination).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_cache = np.asarray(k_cache, dtype=np.float64)
+    v_cache = np.asarray(v_cache, dtype=np.float64)
+    seqlens = np.asarray(seqlens).reshape(-1)
+    B, g_q, d = q.shape
+    Bk, g_kv, n_max, dk = k_cache.shape
+    if (Bk, dk) != (B, d) or v_cache.shape != k_cache.shape or seqlens.shape[0] != B:
+        raise ValueError("inconsistent GQKVA decode shapes")
+    out = np.zeros((B, g_q * g_kv, d), dtype=np.float64)
+    for b in range(B):
+        n = attended_length(seqlens[b], n_max)
+        if n == 0:
+            continue
+        for h in range(g_q * g_kv):
+            i, j = gqkva_head_pair(h, g_q, g_kv)
+            out[b, h] = attend_one_query(q[b, i], k_cache[b, j, :n], v_cache[b, j, :n], scale)
+    return out
+
+
+def gqkva_prefill_causal_ref(q, k, v, scale: float, rows=None) -> np.ndarray:
+    """Causal GQKVA over a prompt, in float64.  Returns out[B, T, g_q * g_kv, d].
+
+    q: [B, T, g_q, d]; k, v: [B, T, g_kv, d].  Position t of output head
+    h = (i, j) attends keys 0..t of K/V group j with query group i's query.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, T, g_q, d = q.shape
+    g_kv = k.shape[2]
+    if k.shape != (B, T, g_kv, d) or v.shape != k.shape:
+        raise ValueError("inconsistent GQKVA prefill shapes")
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1)
+    out = np.full((B, T, g_q * g_kv, d), np.nan, dtype=np.float64)
+    future = future_keys(rows, T)
+    for b in range(B):
+        for h in range(g_q * g_kv):
+            i, j = gqkva_head_pair(h, g_q, g_kv)
+            scores = float(scale) * (q[b, rows, i, :] @ k[b, :, j, :].T)
+            scores = np.where(future, -np.inf, scores)
+            out[b, rows, h, :] = softmax_weights(scores) @ v[b, :, j, :]
     return out
 
 

@@ -375,6 +375,114 @@ def pin_append_single_token(seed=17):
             assert np.array_equal(out[b, h], v_new[b, h // (H // G)])
 
 
+def pin_chunk_vs_sdpa_mask(seed=18):
+    """A chunk after ctx cached positions: SDPA with an explicit boolean mask in
+    which row t may see positions 0 .. ctx+t (float64, CPU)."""
+    rng = _rng(seed)
+    B, H, G, d, n_max, Tc = 4, 8, 2, 16, 20, 5
+    scale = 1.0 / math.sqrt(d)
+    q = rng.standard_normal((B, Tc, H, d))
+    kc = rng.standard_normal((B, G, n_max, d))
+    vc = rng.standard_normal((B, G, n_max, d))
+    ctx = [0, 7, 15, 18]                    # the last one runs past the cache: clamped
+    out = oracle.prefill_chunk_ref(q, kc, vc, ctx, scale)
+    for b in range(B):
+        L = min(ctx[b] + Tc, n_max)
+        mask = torch.zeros((Tc, L), dtype=torch.bool)
+        for t in range(Tc):
+            mask[t, :min(ctx[b] + t, n_max - 1) + 1] = True
+        qb = torch.from_numpy(q[b].transpose(1, 0, 2).copy())[None]          # [1, H, Tc, d]
+        kb = torch.from_numpy(kc[b, :, :L].copy())[None]                     # [1, G, L, d]
+        vb = torch.from_numpy(vc[b, :, :L].copy())[None]
+        ref = F.scaled_dot_product_attention(qb, kb, vb, attn_mask=mask, scale=scale, enable_gqa=True)
+        np.testing.assert_allclose(out[b], ref[0].numpy().transpose(1, 0, 2), rtol=1e-12, atol=1e-12)
+
+
+def pin_chunk_single_row_is_decode(seed=19):
+    """A one-position chunk is the decode step with length ctx + 1."""
+    rng = _rng(seed)
+    B, H, G, d, n_max = 3, 8, 4, 8, 12
+    q = rng.standard_normal((B, 1, H, d))
+    kc = rng.standard_normal((B, G, n_max, d))
+    vc = rng.standard_normal((B, G, n_max, d))
+    ctx = [0, 5, 11]
+    out = oracle.prefill_chunk_ref(q, kc, vc, ctx, 0.4)
+    ref = _sdpa_decode(q[:, 0], kc, vc, [c + 1 for c in ctx], 0.4)
+    np.testing.assert_allclose(out[:, 0], ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_chunk_zero_ctx_is_prefill(seed=20):
+    """ctx = 0 with the prompt's K/V in the cache is the whole-prompt causal prefill
+    (torch SDPA with is_causal)."""
+    rng = _rng(seed)
+    B, T, H, G, d = 2, 9, 6, 3, 8
+    q = rng.standard_normal((B, T, H, d))
+    k = rng.standard_normal((B, G, T, d))
+    v = rng.standard_normal((B, G, T, d))
+    out = oracle.prefill_chunk_ref(q, k, v, [0, 0], 0.3)
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q.transpose(0, 2, 1, 3).copy()),
+                                         torch.from_numpy(k), torch.from_numpy(v), is_causal=True,
+                                         scale=0.3, enable_gqa=True)
+    np.testing.assert_allclose(out, ref.numpy().transpose(0, 2, 1, 3), rtol=1e-12, atol=1e-12)
+
+
+def _expand_gqkva(q, k, g_q, g_kv, axis_q, axis_k):
+    """MHA operands of GQKVA: head h takes query group h // g_kv and K/V group h % g_kv."""
+    qi = [h // g_kv for h in range(g_q * g_kv)]
+    kj = [h % g_kv for h in range(g_q * g_kv)]
+    return np.take(q, qi, axis=axis_q), np.take(k, kj, axis=axis_k)
+
+
+def pin_gqkva_vs_sdpa_expanded(seed=21):
+    """GQKVA decode and prefill against plain MHA (torch SDPA) on operands expanded
+    to one (query, K/V) pair per output head."""
+    rng = _rng(seed)
+    B, g_q, g_kv, d, n_max = 3, 2, 3, 8, 10
+    q = rng.standard_normal((B, g_q, d))
+    kc = rng.standard_normal((B, g_kv, n_max, d))
+    vc = rng.standard_normal((B, g_kv, n_max, d))
+    sl = [10, 4, 1]
+    out = oracle.gqkva_decode_ref(q, kc, vc, sl, 0.35)
+    qe, ke = _expand_gqkva(q, kc, g_q, g_kv, 1, 1)
+    _, ve = _expand_gqkva(q, vc, g_q, g_kv, 1, 1)
+    np.testing.assert_allclose(out, _sdpa_decode(qe, ke, ve, sl, 0.35), rtol=1e-12, atol=1e-12)
+    T = 7
+    qp = rng.standard_normal((B, T, g_q, d))
+    kp = rng.standard_normal((B, T, g_kv, d))
+    vp = rng.standard_normal((B, T, g_kv, d))
+    outp = oracle.gqkva_prefill_causal_ref(qp, kp, vp, 0.35)
+    qe, ke = _expand_gqkva(qp, kp, g_q, g_kv, 2, 2)
+    _, ve = _expand_gqkva(qp, vp, g_q, g_kv, 2, 2)
+    ref = F.scaled_dot_product_attention(torch.from_numpy(qe.transpose(0, 2, 1, 3).copy()),
+                                         torch.from_numpy(ke.transpose(0, 2, 1, 3).copy()),
+                                         torch.from_numpy(ve.transpose(0, 2, 1, 3).copy()),
+                                         is_causal=True, scale=0.35)
+    np.testing.assert_allclose(outp, ref.numpy().transpose(0, 2, 1, 3), rtol=1e-12, atol=1e-12)
+
+
+def pin_gqkva_special_cases(seed=22):
+    """Constant V per K/V group j: every head paired with j returns that constant.
+    One query group (MKVA): heads differ only in their K/V group."""
+    rng = _rng(seed)
+    B, g_q, g_kv, d, n_max = 2, 3, 2, 4, 6
+    q = rng.standard_normal((B, g_q, d))
+    kc = rng.standard_normal((B, g_kv, n_max, d))
+    vc = np.empty((B, g_kv, n_max, d))
+    vc[:, 0] = 0.25
+    vc[:, 1] = -1.5
+    out = oracle.gqkva_decode_ref(q, kc, vc, [6, 3], 0.5)
+    for h in range(g_q * g_kv):
+        np.testing.assert_allclose(out[:, h], np.full((B, d), 0.25 if h % g_kv == 0 else -1.5),
+                                   rtol=1e-14, atol=0)
+    v2 = rng.standard_normal((B, g_kv, n_max, d))
+    q1 = q[:, :1]
+    out1 = oracle.gqkva_decode_ref(q1, kc, v2, [6, 3], 0.5)
+    for j in range(g_kv):
+        for b, n in enumerate([6, 3]):
+            want = oracle.attend_one_query(q1[b, 0], kc[b, j, :n], v2[b, j, :n], 0.5)
+            assert np.array_equal(out1[b, j], want)
+
+
 def pin_flop_counts():
     # Decode operations do not depend on G (blog, "MQA 的推导": the arithmetic is unchanged)
     assert oracle.decode_flops(32, 16 * 1024, 128) == 268435456
@@ -389,7 +497,9 @@ PINS = [
     pin_mqa_vs_sdpa_broadcast, pin_brute_force, pin_single_key, pin_constant_values,
     pin_zero_query_is_mean, pin_two_keys_sigmoid, pin_repeat_kv, pin_tail_ignored,
     pin_permutation, pin_prefill_vs_sdpa, pin_prefill_rows_are_decodes, pin_meanpool,
-    pin_append_vs_sdpa_concat, pin_append_cache_rows, pin_append_single_token, pin_flop_counts,
+    pin_append_vs_sdpa_concat, pin_append_cache_rows, pin_append_single_token,
+    pin_chunk_vs_sdpa_mask, pin_chunk_single_row_is_decode, pin_chunk_zero_ctx_is_prefill,
+    pin_gqkva_vs_sdpa_expanded, pin_gqkva_special_cases, pin_flop_counts,
 ]
 
 
@@ -506,3 +616,16 @@ def test_mutation_append_skipped_caught(monkeypatch):
     monkeypatch.setattr(og, "append_position", lambda s, n: None)
     failed = _fails([pin_append_vs_sdpa_concat, pin_append_cache_rows, pin_append_single_token])
     assert len(failed) == 3
+
+
+def test_mutation_chunk_off_by_one_caught(monkeypatch):
+    monkeypatch.setattr(og, "chunk_attended_length",
+                        lambda c, t, n: int(min(max(int(c), 0) + int(t), int(n))))
+    failed = _fails([pin_chunk_vs_sdpa_mask, pin_chunk_single_row_is_decode, pin_chunk_zero_ctx_is_prefill])
+    assert len(failed) == 3
+
+
+def test_mutation_gqkva_pairing_swapped_caught(monkeypatch):
+    monkeypatch.setattr(og, "gqkva_head_pair", lambda h, gq, gkv: (h % gq, h // gq))
+    failed = _fails([pin_gqkva_vs_sdpa_expanded, pin_gqkva_special_cases])
+    assert "pin_gqkva_vs_sdpa_expanded" in failed and "pin_gqkva_special_cases" in failed
