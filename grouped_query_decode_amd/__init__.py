@@ -9,6 +9,9 @@ library is missing, every call raises.
     decode(q, k_cache, v_cache, seqlens)        # one decode step, [B,H,d]
     decode_append(q, k_new, v_new, k_cache, v_cache, seqlens)  # append, then decode
     prefill_causal(q, k, v)                     # causal prefill, [B,T,H,d]
+    prefill_chunk(q, k_cache, v_cache, ctx_lens) # a prompt chunk after ctx cached positions
+    gqkva_decode(q, k_cache, v_cache, seqlens)  # all query-group x K/V-group pairs
+    gqkva_prefill_causal(q, k, v)
     meanpool_heads(w, G)                        # MHA -> GQA K/V conversion
 """
 
@@ -22,7 +25,8 @@ import torch
 
 __all__ = [
     "GQAError", "library_path", "load_library", "decode", "decode_append", "decode_num_splits",
-    "decode_workspace_bytes", "prefill_causal", "meanpool_heads", "DTYPE_CODES",
+    "decode_workspace_bytes", "prefill_causal", "prefill_chunk", "gqkva_decode",
+    "gqkva_prefill_causal", "meanpool_heads", "DTYPE_CODES",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +76,14 @@ def load_library():
     lib.gqa_decode_append.restype = i32
     lib.gqa_prefill_causal.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.gqa_prefill_causal.restype = i32
+    lib.gqa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.gqa_prefill_chunk.restype = i32
+    lib.gqkva_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, sz, vp]
+    lib.gqkva_decode.restype = i32
+    lib.gqkva_decode_workspace_bytes.argtypes = [i32] * 6
+    lib.gqkva_decode_workspace_bytes.restype = sz
+    lib.gqkva_prefill_causal.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.gqkva_prefill_causal.restype = i32
     lib.kv_meanpool_heads.argtypes = [vp, vp, i32, i32, i64, i32, vp]
     lib.kv_meanpool_heads.restype = i32
     lib.gqa_status_string.argtypes = [i32]
@@ -253,6 +265,113 @@ def prefill_causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: flo
     st = lib.gqa_prefill_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, H, G, d, float(scale),
                                 _dtype_code(q), ctypes.c_void_p(_stream_handle(dev)))
     _check("gqa_prefill_causal", st)
+    return out
+
+
+def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, ctx_lens: torch.Tensor,
+                  scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """A prompt chunk after ctx_lens[b] cached positions: q [B,T,H,d],
+    k_cache/v_cache [B,G,Nmax,d] (the chunk's K/V already at ctx..ctx+T-1),
+    ctx_lens [B] int32 -> out [B,T,H,d]; row t sees positions 0..ctx+t."""
+    lib = load_library()
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q must be [B,T,H,d] and k_cache [B,G,Nmax,d]")
+    B, T, H, d = q.shape
+    Bk, G, n_max, dk = k_cache.shape
+    if (Bk, dk) != (B, d) or v_cache.shape != k_cache.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k_cache.shape)}")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    if ctx_lens.dtype != torch.int32 or ctx_lens.shape != (B,):
+        raise ValueError("ctx_lens must be an int32 tensor of shape [B]")
+    dev = q.device
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("ctx_lens", ctx_lens)):
+        _require_device(name, t, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require_device("out", out, dev)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.gqa_prefill_chunk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_lens), _ptr(out),
+                               B, T, H, G, d, n_max, float(scale), _dtype_code(q),
+                               ctypes.c_void_p(_stream_handle(dev)))
+    _check("gqa_prefill_chunk", st)
+    return out
+
+
+def gqkva_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlens: torch.Tensor,
+                 scale: float | None = None, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None, num_splits: int = 0) -> torch.Tensor:
+    """GQKVA decode: q [B,g_q,d], caches [B,g_kv,Nmax,d] -> out [B, g_q*g_kv, d]; output
+    head h pairs query group h // g_kv with K/V group h % g_kv."""
+    lib = load_library()
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B,g_q,d] and k_cache [B,g_kv,Nmax,d]")
+    B, g_q, d = q.shape
+    Bk, g_kv, n_max, dk = k_cache.shape
+    if (Bk, dk) != (B, d) or v_cache.shape != k_cache.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k_cache.shape)}")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    if seqlens.dtype != torch.int32 or seqlens.shape != (B,):
+        raise ValueError("seqlens must be an int32 tensor of shape [B]")
+    dev = q.device
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seqlens", seqlens)):
+        _require_device(name, t, dev)
+    shape = (B, g_q * g_kv, d)
+    if out is None:
+        out = torch.empty(shape, dtype=q.dtype, device=dev)
+    else:
+        _require_device("out", out, dev)
+        if out.shape != shape or out.dtype != q.dtype:
+            raise ValueError("out must be [B, g_q*g_kv, d] in q's dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = 0
+    if B > 0:
+        need = lib.gqkva_decode_workspace_bytes(B, g_q, g_kv, d, n_max, num_splits)
+        if need == ctypes.c_size_t(-1).value:
+            raise ValueError("invalid GQKVA decode shape")
+    if need > 0 and workspace is None:
+        workspace = _cached_workspace(dev, need)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gqkva_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(out), B, g_q,
+                          g_kv, d, n_max, float(scale), _dtype_code(q), int(num_splits),
+                          _ptr(workspace), ws_bytes, ctypes.c_void_p(_stream_handle(dev)))
+    _check("gqkva_decode", st)
+    return out
+
+
+def gqkva_prefill_causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """Causal GQKVA prefill: q [B,T,g_q,d], k/v [B,T,g_kv,d] -> out [B,T,g_q*g_kv,d]."""
+    lib = load_library()
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B,T,g_q,d] and k, v [B,T,g_kv,d]")
+    B, T, g_q, d = q.shape
+    Bk, Tk, g_kv, dk = k.shape
+    if (Bk, Tk, dk) != (B, T, d) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require_device(name, t, dev)
+    shape = (B, T, g_q * g_kv, d)
+    if out is None:
+        out = torch.empty(shape, dtype=q.dtype, device=dev)
+    else:
+        _require_device("out", out, dev)
+        if out.shape != shape or out.dtype != q.dtype:
+            raise ValueError("out must be [B, T, g_q*g_kv, d] in q's dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.gqkva_prefill_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, g_q, g_kv, d,
+                                  float(scale), _dtype_code(q), ctypes.c_void_p(_stream_handle(dev)))
+    _check("gqkva_prefill_causal", st)
     return out
 
 

@@ -107,10 +107,13 @@ gqa_status launched(hipError_t e, const char* what) {
   return ok();
 }
 
+// H query heads (GQA) or, with gqkva, H = g_q query groups paired with every
+// one of the G K/V groups (H*G outputs).
 gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_t* seqlens,
                        void* out, int B, int H, int G, int d, int n_max, float scale, int dtype,
                        int num_splits, void* ws, size_t ws_bytes, void* stream_v,
-                       const void* k_new = nullptr, const void* v_new = nullptr) {
+                       const void* k_new = nullptr, const void* v_new = nullptr,
+                       bool gqkva = false) {
   g_last_error.clear();
   const bool append = k_new != nullptr || v_new != nullptr;
   if (!known_dtype(dtype)) return fail(GQA_ERR_INVALID_ARG, "gqa_decode: unknown dtype %d", dtype);
@@ -119,9 +122,15 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
   if (B == 0) return ok();
   if (H < 1 || G < 1)
     return fail(GQA_ERR_INVALID_ARG, "gqa_decode: H=%d and G=%d must be >= 1", H, G);
-  if (H % G != 0)
+  if (!gqkva && H % G != 0)
     return fail(GQA_ERR_INVALID_ARG, "gqa_decode: H=%d is not a multiple of G=%d", H, G);
   if (d < 1) return fail(GQA_ERR_INVALID_ARG, "gqa_decode: head size d=%d", d);
+  if (gqkva && int64_t(H) * G > (int64_t(1) << 20))
+    return fail(GQA_ERR_INVALID_ARG, "gqkva_decode: too many query x K/V groups");
+  // n_rep queries per K/V head; Hp = G * n_rep rows of partial results per sequence
+  const int n_rep = gqkva ? H : H / G;
+  const int Hp = G * n_rep;
+  const gqa::HeadMap hm = gqkva ? gqa::gqkva_head_map(H, G) : gqa::gqa_head_map(G, n_rep);
   if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "gqa_decode: scale is not finite");
   if (num_splits < 0) return fail(GQA_ERR_INVALID_ARG, "gqa_decode: num_splits=%d", num_splits);
   if (!q || !out || !seqlens || (n_max > 0 && (!k || !v)) || (append && (!k_new || !v_new)))
@@ -133,14 +142,14 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
     return fail(GQA_ERR_INVALID_ARG, "gqa_decode: tensors must be 16-byte aligned");
   if (d != 64 && d != 128)
     return fail(GQA_ERR_UNSUPPORTED, "gqa_decode: head size d=%d (built for 64 and 128)", d);
-  const int64_t n_rows64 = int64_t(B) * H;
+  const int64_t n_rows64 = int64_t(B) * Hp;
   if (n_rows64 * d > (int64_t(1) << 40) || int64_t(B) * G * n_max > (int64_t(1) << 40))
     return fail(GQA_ERR_INVALID_ARG, "gqa_decode: problem too large");
 
   int S_req = num_splits == 0 ? plan_splits(B, G, n_max) : std::min(num_splits, std::max(n_max, 1));
   int S, split_len;
   split_geometry(n_max, S_req, &S, &split_len);
-  const size_t need = workspace_for(B, H, d, S);
+  const size_t need = workspace_for(B, Hp, d, S);
   if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned16(ws)))
     return fail(GQA_ERR_WORKSPACE, "gqa_decode: workspace of %zu bytes needed, %zu given%s", need,
                 ws_bytes, (ws && !aligned16(ws)) ? " (misaligned)" : "");
@@ -152,11 +161,10 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
     char* base = static_cast<char*>(ws);
     counters = reinterpret_cast<int*>(base);
     part_o = reinterpret_cast<float*>(base + kCounterBytes);
-    const size_t o_bytes = partial_o_bytes(B, H, d, S);
+    const size_t o_bytes = partial_o_bytes(B, Hp, d, S);
     part_ml = reinterpret_cast<float*>(base + kCounterBytes + ((o_bytes + 255) / 256) * 256);
   }
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
-  const int n_rep = H / G;
 
   if (dtype != GQA_DTYPE_F32 && gqa::decode_mfma_supports(n_rep, d, S, split_len)) {
     gqa::DecodeProblem p{};
@@ -172,7 +180,8 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
     p.k_new = static_cast<const uint16_t*>(k_new);
     p.v_new = static_cast<const uint16_t*>(v_new);
     p.dtype = dtype;
-    p.B = B; p.H = H; p.G = G; p.n_rep = n_rep; p.d = d; p.n_max = n_max;
+    p.hm = hm;
+    p.B = B; p.H = Hp; p.G = G; p.n_rep = n_rep; p.d = d; p.n_max = n_max;
     p.scale = scale;
     p.num_splits = S;
     p.split_len = split_len;
@@ -192,8 +201,8 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
     p.q = q; p.k = k; p.v = v; p.seqlens = seqlens; p.out = out;
     p.part_o = part_o; p.part_ml = part_ml;
     p.n_rows = B; p.rows_per_batch = 1;
-    p.H = H; p.G = G; p.n_rep = n_rep; p.d = d;
-    p.q_row_stride = int64_t(H) * d;
+    p.H = Hp; p.G = G; p.n_rep = n_rep; p.d = d;
+    p.hm = hm;
     p.kv_batch_stride = int64_t(G) * n_max * d;
     p.kv_group_stride = int64_t(n_max) * d;
     p.kv_pos_stride = d;
@@ -208,10 +217,79 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
   if (S > 1) {
     gqa::CombineProblem c{};
     c.part_o = part_o; c.part_ml = part_ml; c.out = out;
-    c.n_rows = B; c.H = H; c.d = d; c.num_splits = S; c.dtype = dtype;
+    c.n_rows = B; c.H = Hp; c.d = d; c.num_splits = S; c.dtype = dtype;
+    c.n_rep = n_rep; c.hm = hm;
     return launched(gqa::launch_combine(c, stream), "gqa_decode (combine)");
   }
   return ok();
+}
+
+// Causal attention of T query rows per sequence.  Prompt layout (kv_cap = T,
+// K/V [B, T, G, d], ctx_lens null) or cache layout (K/V [B, G, n_max, d],
+// row t at position ctx_lens[b] + t).  gqkva: H query groups x G K/V groups.
+gqa_status prefill_impl(const char* name, const void* q, const void* k, const void* v, void* out,
+                        const int32_t* ctx_lens, bool cache_layout, int B, int T, int H, int G,
+                        int d, int n_max, float scale, int dtype, void* stream_v, bool gqkva) {
+  g_last_error.clear();
+  if (!known_dtype(dtype)) return fail(GQA_ERR_INVALID_ARG, "%s: unknown dtype %d", name, dtype);
+  if (B < 0 || T < 0 || n_max < 0)
+    return fail(GQA_ERR_INVALID_ARG, "%s: negative size (B=%d, T=%d, n_max=%d)", name, B, T, n_max);
+  if (B == 0 || T == 0) return ok();
+  if (H < 1 || G < 1) return fail(GQA_ERR_INVALID_ARG, "%s: H=%d and G=%d must be >= 1", name, H, G);
+  if (!gqkva && H % G != 0)
+    return fail(GQA_ERR_INVALID_ARG, "%s: H=%d is not a multiple of G=%d", name, H, G);
+  if (cache_layout && n_max < 1)
+    return fail(GQA_ERR_INVALID_ARG, "%s: n_max=%d leaves no room for the chunk", name, n_max);
+  if (d < 1) return fail(GQA_ERR_INVALID_ARG, "%s: head size d=%d", name, d);
+  if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "%s: scale is not finite", name);
+  if (!q || !k || !v || !out || (cache_layout && !ctx_lens))
+    return fail(GQA_ERR_INVALID_ARG, "%s: NULL tensor", name);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(ctx_lens) & 3u))
+    return fail(GQA_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", name);
+  if (d != 64 && d != 128)
+    return fail(GQA_ERR_UNSUPPORTED, "%s: head size d=%d (built for 64 and 128)", name, d);
+  const int n_rep = gqkva ? H : H / G;
+  const int64_t out_heads = int64_t(G) * n_rep;
+  if (int64_t(B) * T * out_heads * d > (int64_t(1) << 40) ||
+      (cache_layout && int64_t(B) * G * n_max * d > (int64_t(1) << 40)))
+    return fail(GQA_ERR_INVALID_ARG, "%s: problem too large", name);
+  const gqa::HeadMap hm = gqkva ? gqa::gqkva_head_map(H, G) : gqa::gqa_head_map(G, n_rep);
+  const int kv_cap = cache_layout ? n_max : T;
+  const int64_t kv_b = cache_layout ? int64_t(G) * n_max * d : int64_t(T) * G * d;
+  const int64_t kv_g = cache_layout ? int64_t(n_max) * d : d;
+  const int64_t kv_p = cache_layout ? d : int64_t(G) * d;
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  if (dtype != GQA_DTYPE_F32 && gqa::prefill_mfma_supports(n_rep, d)) {
+    gqa::PrefillProblem p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.out = static_cast<uint16_t*>(out);
+    p.ctx_lens = ctx_lens;
+    p.dtype = dtype;
+    p.hm = hm;
+    p.kv_bstride = kv_b; p.kv_gstride = kv_g; p.kv_pstride = kv_p;
+    p.kv_cap = kv_cap;
+    p.B = B; p.T = T; p.G = G; p.n_rep = n_rep; p.d = d;
+    p.scale = scale;
+    return launched(gqa::launch_prefill_mfma(p, stream), name);
+  }
+  gqa::RowsProblem p{};
+  p.q = q; p.k = k; p.v = v; p.seqlens = nullptr; p.out = out;
+  p.n_rows = B * T; p.rows_per_batch = T;
+  p.H = int(out_heads); p.G = G; p.n_rep = n_rep; p.d = d;
+  p.hm = hm;
+  p.ctx_lens = ctx_lens;
+  p.kv_batch_stride = kv_b;
+  p.kv_group_stride = kv_g;
+  p.kv_pos_stride = kv_p;
+  p.n_max = kv_cap;
+  p.causal = 1;
+  p.scale = scale;
+  p.num_splits = 1;
+  p.split_len = kv_cap;
+  return launched(gqa::launch_rows_valu(p, dtype, stream), name);
 }
 
 }  // namespace
@@ -262,54 +340,39 @@ gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new
 }
 
 gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void* out, int B,
-                              int T, int H, int G, int d, float scale, int dtype, void* stream_v) {
-  g_last_error.clear();
-  if (!known_dtype(dtype))
-    return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: unknown dtype %d", dtype);
-  if (B < 0 || T < 0)
-    return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: negative size (B=%d, T=%d)", B, T);
-  if (B == 0 || T == 0) return ok();
-  if (H < 1 || G < 1)
-    return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: H=%d and G=%d must be >= 1", H, G);
-  if (H % G != 0)
-    return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: H=%d is not a multiple of G=%d", H, G);
-  if (d < 1) return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: head size d=%d", d);
-  if (!std::isfinite(scale))
-    return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: scale is not finite");
-  if (!q || !k || !v || !out) return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: NULL tensor");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: tensors must be 16-byte aligned");
-  if (d != 64 && d != 128)
-    return fail(GQA_ERR_UNSUPPORTED, "gqa_prefill_causal: head size d=%d (built for 64 and 128)", d);
-  if (int64_t(B) * T * H * d > (int64_t(1) << 40))
-    return fail(GQA_ERR_INVALID_ARG, "gqa_prefill_causal: problem too large");
-  hipStream_t stream = static_cast<hipStream_t>(stream_v);
-  const int n_rep = H / G;
-  if (dtype != GQA_DTYPE_F32 && gqa::prefill_mfma_supports(n_rep, d)) {
-    gqa::PrefillProblem p{};
-    p.q = static_cast<const uint16_t*>(q);
-    p.k = static_cast<const uint16_t*>(k);
-    p.v = static_cast<const uint16_t*>(v);
-    p.out = static_cast<uint16_t*>(out);
-    p.B = B; p.T = T; p.H = H; p.G = G; p.n_rep = n_rep; p.d = d;
-    p.scale = scale;
-    p.dtype = dtype;
-    return launched(gqa::launch_prefill_mfma(p, stream), "gqa_prefill_causal");
-  }
-  gqa::RowsProblem p{};
-  p.q = q; p.k = k; p.v = v; p.seqlens = nullptr; p.out = out;
-  p.n_rows = B * T; p.rows_per_batch = T;
-  p.H = H; p.G = G; p.n_rep = n_rep; p.d = d;
-  p.q_row_stride = int64_t(H) * d;
-  p.kv_batch_stride = int64_t(T) * G * d;
-  p.kv_group_stride = d;
-  p.kv_pos_stride = int64_t(G) * d;
-  p.n_max = T;
-  p.causal = 1;
-  p.scale = scale;
-  p.num_splits = 1;
-  p.split_len = T;
-  return launched(gqa::launch_rows_valu(p, dtype, stream), "gqa_prefill_causal");
+                              int T, int H, int G, int d, float scale, int dtype, void* stream) {
+  return prefill_impl("gqa_prefill_causal", q, k, v, out, nullptr, false, B, T, H, G, d, 0, scale,
+                      dtype, stream, false);
+}
+
+gqa_status gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* ctx_lens, void* out, int B, int T, int H, int G, int d,
+                             int n_max, float scale, int dtype, void* stream) {
+  return prefill_impl("gqa_prefill_chunk", q, k_cache, v_cache, out, ctx_lens, true, B, T, H, G, d,
+                      n_max, scale, dtype, stream, false);
+}
+
+gqa_status gqkva_prefill_causal(const void* q, const void* k, const void* v, void* out, int B,
+                                int T, int g_q, int g_kv, int d, float scale, int dtype,
+                                void* stream) {
+  return prefill_impl("gqkva_prefill_causal", q, k, v, out, nullptr, false, B, T, g_q, g_kv, d, 0,
+                      scale, dtype, stream, true);
+}
+
+gqa_status gqkva_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seqlens, void* out, int B, int g_q, int g_kv, int d,
+                        int n_max, float scale, int dtype, int num_splits, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, seqlens, out, B, g_q, g_kv, d, n_max, scale, dtype,
+                     num_splits, workspace, workspace_bytes, stream, nullptr, nullptr, true);
+}
+
+size_t gqkva_decode_workspace_bytes(int B, int g_q, int g_kv, int d, int n_max, int num_splits) {
+  if (B < 0 || n_max < 0 || d < 1 || num_splits < 0 || g_q < 1 || g_kv < 1) return size_t(-1);
+  int S_req = num_splits == 0 ? plan_splits(B, g_kv, n_max) : std::min(num_splits, std::max(n_max, 1));
+  int S, len;
+  split_geometry(n_max, S_req, &S, &len);
+  return workspace_for(B, g_q * g_kv, d, S);
 }
 
 gqa_status kv_meanpool_heads(const void* w_in, void* w_out, int H, int G, int64_t per_head_elems,

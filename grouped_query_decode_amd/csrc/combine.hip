@@ -37,7 +37,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineProblem p) {
       }
     }
     const float val = L > 0.f ? O / L : 0.f;
-    const int64_t oi = pair * p.d + col;
+    const int64_t row = pair / p.H;
+    const int h = int(pair - row * p.H);
+    const int64_t oi = (row * p.hm.o_heads + p.hm.o_head(h / p.n_rep, h % p.n_rep)) * p.d + col;
     if (DT == kF32)
       static_cast<float*>(p.out)[oi] = val;
     else if (DT == kF16)

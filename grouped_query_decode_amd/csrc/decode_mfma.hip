@@ -111,7 +111,7 @@ struct UnitPartials {
 // rescaled per batch.
 template <int D, int DT>
 __device__ __forceinline__ void merge_item(const DecodeProblem& p, const UnitPartials<D>& up, int b, int ns,
-                                           int h, int hl, int c8) {
+                                           int g, int hl, int c8) {
   using H16 = Half16<DT>;
   const int S = p.num_splits;
   float M = -INFINITY, L = 0.f;
@@ -150,7 +150,7 @@ __device__ __forceinline__ void merge_item(const DecodeProblem& p, const UnitPar
     M = cm;
   }
   const float inv = L > 0.f ? __builtin_amdgcn_rcpf(L) : 0.f;
-  st16(p.out + (int64_t(b) * p.H + h) * D + c8 * 8,
+  st16(p.out + (int64_t(b) * p.hm.o_heads + p.hm.o_head(g, hl)) * D + c8 * 8,
        u32x4_t{H16::pack2(Oa[0] * inv, Oa[1] * inv), H16::pack2(Oa[2] * inv, Oa[3] * inv),
                H16::pack2(Ob[0] * inv, Ob[1] * inv), H16::pack2(Ob[2] * inv, Ob[3] * inv)});
 }
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   for (int hb = 0; hb < NHB; ++hb) {
     const int hl = hb * 16 + lo;
     const bool hv = hl < p.n_rep;
-    const uint16_t* qrow = p.q + (int64_t(b) * p.H + g * p.n_rep + (hv ? hl : 0)) * D;
+    const uint16_t* qrow = p.q + (int64_t(b) * p.hm.q_heads + p.hm.q_head(g, hv ? hl : 0)) * D;
 #pragma unroll
     for (int ks = 0; ks < C::kSteps; ++ks) {
       u32x4_t w = {0u, 0u, 0u, 0u};
@@ -434,10 +434,9 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
           O += f * *reinterpret_cast<const f32x4_t*>(sm_o + (w * 16 + hl) * C::kMergeRow + c4 * 4);
         }
       }
-      const int h = g * p.n_rep + 16 * hb + hl;
       if (ns == 1) {
         const float inv = L > 0.f ? __builtin_amdgcn_rcpf(L) : 0.f;
-        *reinterpret_cast<uint2*>(p.out + (int64_t(b) * p.H + h) * D + c4 * 4) =
+        *reinterpret_cast<uint2*>(p.out + (int64_t(b) * p.hm.o_heads + p.hm.o_head(g, 16 * hb + hl)) * D + c4 * 4) =
             make_uint2(H16::pack2(O[0] * inv, O[1] * inv), H16::pack2(O[2] * inv, O[3] * inv));
       } else {
         const int pr = (16 * hb + hl) * S + s;       // within the unit's partials
@@ -468,7 +467,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   constexpr int kC8 = D / 8;
 #pragma unroll 1
   for (int t = threadIdx.x; t < p.n_rep * kC8; t += blockDim.x)
-    merge_item<D, DT>(p, up, b, ns, g * p.n_rep + t / kC8, t / kC8, t % kC8);
+    merge_item<D, DT>(p, up, b, ns, g, t / kC8, t % kC8);
 }
 
 template <int D, int NHB, int DT>

@@ -8,6 +8,23 @@ namespace gqa {
 
 enum Dtype { kF32 = 0, kBF16 = 1, kF16 = 2 };
 
+// Which query row feeds, and which output row receives, query r (0 .. n_rep-1)
+// of K/V head g.  GQA: q head g*n_rep + r and the same output head.  GQKVA
+// (every query group with every K/V group): q head r, output head r*G + g.
+struct HeadMap {
+  int q_heads, q_g, q_r;    // q head = g*q_g + r*q_r, q_heads per token row
+  int o_heads, o_g, o_r;    // out head = g*o_g + r*o_r, o_heads per token row
+  __host__ __device__ int64_t q_head(int g, int r) const { return int64_t(g) * q_g + int64_t(r) * q_r; }
+  __host__ __device__ int64_t o_head(int g, int r) const { return int64_t(g) * o_g + int64_t(r) * o_r; }
+};
+
+inline HeadMap gqa_head_map(int G, int n_rep) {
+  return HeadMap{G * n_rep, n_rep, 1, G * n_rep, n_rep, 1};
+}
+inline HeadMap gqkva_head_map(int g_q, int g_kv) {
+  return HeadMap{g_q, 0, 1, g_q * g_kv, 1, g_kv};
+}
+
 // Generic "rows of queries attend a K/V head" problem, used by the vector-unit
 // kernel for decode (one row per sequence) and for float32 causal prefill (one
 // row per prompt position).  All strides are in elements.
@@ -21,13 +38,14 @@ struct RowsProblem {
   float* part_ml;           // [rows, H, S, 2] (running max, normaliser), when S > 1
   int n_rows;               // decode: B; prefill: B*T
   int rows_per_batch;       // decode: 1; prefill: T
-  int H, G, n_rep, d;
-  int64_t q_row_stride;     // between consecutive rows (q and out)
+  int H, G, n_rep, d;       // H = G*n_rep (the partial results' layout)
+  HeadMap hm;               // q / out rows of (g, r); rows are hm.q_heads*d / hm.o_heads*d apart
+  const int32_t* ctx_lens;  // causal: positions before row 0 of each batch (null: none)
   int64_t kv_batch_stride;  // between batches
   int64_t kv_group_stride;  // between K/V heads
   int64_t kv_pos_stride;    // between cached positions
   int n_max;                // decode: cache capacity; prefill: T
-  int causal;               // 0: length from seqlens; 1: row i attends 0..i
+  int causal;               // 0: length from seqlens; 1: row i attends 0..ctx+i
   float scale;
   int num_splits;           // S
   int split_len;            // positions per split
@@ -46,7 +64,8 @@ struct DecodeProblem {
   const uint16_t* k_new;    // [B, G, d] this step's k, v to append at seqlens[b]-1, or null
   const uint16_t* v_new;
   int dtype;                // kBF16 or kF16
-  int B, H, G, n_rep, d, n_max;
+  HeadMap hm;
+  int B, H, G, n_rep, d, n_max;   // H = G*n_rep (the partial results' layout)
   float scale;
   int num_splits, split_len;
 };
@@ -54,18 +73,27 @@ struct DecodeProblem {
 struct CombineProblem {
   const float* part_o;
   const float* part_ml;
-  void* out;                // [rows, H, d] in dtype
+  void* out;                // rows of hm.o_heads*d elements, in dtype
   int n_rows, H, d, num_splits;
+  int n_rep;                // partial head h = g*n_rep + r goes to out head hm.o_head(g, r)
+  HeadMap hm;
   int dtype;
 };
 
+// Causal attention of T query rows per sequence on the matrix cores.  Row t
+// of sequence b sits at position ctx_b + t (ctx_b = ctx_lens[b], or 0) and
+// attends positions 0 .. min(ctx_b + t, kv_cap - 1) of its K/V head.
 struct PrefillProblem {
-  const uint16_t* q;        // [B, T, H, d]
-  const uint16_t* k;        // [B, T, G, d]
+  const uint16_t* q;        // [B, T, hm.q_heads, d]
+  const uint16_t* k;        // position j of (b, g) at b*kv_bstride + g*kv_gstride + j*kv_pstride
   const uint16_t* v;
-  uint16_t* out;            // [B, T, H, d]
+  uint16_t* out;            // [B, T, hm.o_heads, d]
+  const int32_t* ctx_lens;  // [B] or null
   int dtype;                // kBF16 or kF16
-  int B, T, H, G, n_rep, d;
+  HeadMap hm;
+  int64_t kv_bstride, kv_gstride, kv_pstride;
+  int kv_cap;               // positions that exist per (b, g)
+  int B, T, G, n_rep, d;
   float scale;
 };
 

@@ -119,11 +119,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   const int g = (unit / n_hq) % p.G;
   const int b = unit / (n_hq * p.G);
 
-  const int head = g * p.n_rep + hq * nre + (wave % nre);
+  const int qr = hq * nre + (wave % nre);          // query of the group this wave owns
   const int t_base = qt * rows_wg + (wave / nre) * kQT;
-  const int t_row = t_base + l32;                  // this lane's query position
+  const int t_row = t_base + l32;                  // this lane's query row
   const int t_last = min(p.T, (qt + 1) * rows_wg) - 1;
-  const int n_kt = t_last / kKT + 1;
+  // Row t sits at position ctx + t and sees positions 0 .. min(ctx + t, kv_cap - 1).
+  const int ctx = p.ctx_lens ? max(p.ctx_lens[b], 0) : 0;
+  const int last_pos = p.kv_cap - 1;
+  const int a_row = min(ctx + t_row, last_pos);            // this lane's last visible position
+  const int a_wave = min(ctx + t_base + kQT - 1, last_pos); // ... of the wave's last row
+  const int kv_end = min(ctx + t_last, last_pos) + 1;       // positions any row here sees
+  const int n_kt = (kv_end + kKT - 1) / kKT;
 
   // queries: B operand, lane column = row l32, k-slot group h2 -> dims 16*ks + 8*h2 .. +7.
   // A negative scale is folded into the queries (exact sign flip).
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   u32x4_t qop[C::kSteps];
   {
     const bool rv = t_row < p.T;
-    const uint16_t* qrow = p.q + ((int64_t(b) * p.T + (rv ? t_row : 0)) * p.H + head) * D;
+    const uint16_t* qrow = p.q + ((int64_t(b) * p.T + (rv ? t_row : 0)) * p.hm.q_heads + p.hm.q_head(g, qr)) * D;
 #pragma unroll
     for (int ks = 0; ks < C::kSteps; ++ks) {
       u32x4_t w = {0u, 0u, 0u, 0u};
@@ -152,9 +158,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   float mrun = -INFINITY;     // running max of the raw scores of this lane's row
   float lrun = 0.f;           // this lane's share of the normaliser
 
-  const int64_t kv_row = int64_t(p.G) * D;           // elements between positions
-  const uint16_t* kbase = p.k + (int64_t(b) * p.T * p.G + g) * D;
-  const uint16_t* vbase = p.v + (int64_t(b) * p.T * p.G + g) * D;
+  const int64_t kv_row = p.kv_pstride;               // elements between positions
+  const uint16_t* kbase = p.k + int64_t(b) * p.kv_bstride + int64_t(g) * p.kv_gstride;
+  const uint16_t* vbase = p.v + int64_t(b) * p.kv_bstride + int64_t(g) * p.kv_gstride;
 
   u32x4_t kreg[kLoads];
   // thread's first (position, chunk) of a tile; the others are kRowStep positions apart
@@ -164,14 +170,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   auto load_rows = [&](const uint16_t* base, int kt, u32x4_t* reg) {
     const int key0 = kt * kKT + kl0;
     const uint16_t* ptr = base + int64_t(key0) * kv_row + ch0 * 8;
-    if (kt * kKT + kKT <= p.T) {                   // whole tile inside the prompt
+    if (kt * kKT + kKT <= kv_end) {                // whole tile seen by some row here
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) reg[i] = ld16(ptr + int64_t(i * kRowStep) * kv_row);
     } else {
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         u32x4_t w = {0u, 0u, 0u, 0u};
-        if (key0 + i * kRowStep < p.T) w = ld16(ptr + int64_t(i * kRowStep) * kv_row);
+        if (key0 + i * kRowStep < kv_end) w = ld16(ptr + int64_t(i * kRowStep) * kv_row);
         reg[i] = w;
       }
     }
@@ -192,8 +198,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
       u32x4_t w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
       if (item < kVPairItems) {
         const uint16_t* ptr = vbase + int64_t(key) * kv_row + ch * 8;
-        if (key < p.T) w0 = ld16(ptr);
-        if (key + 1 < p.T) w1 = ld16(ptr + kv_row);
+        if (key < kv_end) w0 = ld16(ptr);
+        if (key + 1 < kv_end) w1 = ld16(ptr + kv_row);
       }
       vpr[j][0] = w0;
       vpr[j][1] = w1;
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          if (key > t_row || key >= p.T) sc[kb][r] = -INFINITY;
+          if (key > a_row) sc[kb][r] = -INFINITY;
         }
     }
     float tmax = mrun;
@@ -315,7 +321,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   // the global loads of K(t+2) and V(t) land in the slots t&1 this iteration
   // freed.  Tiles before t_split lie wholly below every row of the workgroup
   // (no mask) and have a successor; the rest take the masked path.
-  const int t_split = min(n_kt - 1, (qt * rows_wg) / kKT);
+  const int t_split = min(n_kt - 1, min(ctx + qt * rows_wg, last_pos) / kKT);
   load_rows(kbase, 0, kreg);
   store_rows(kslot(0), C::kKPitch, kreg);
   if (n_kt > 1) {
@@ -353,10 +359,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
     if (rescale_prev) rescale_acc(alpha_prev);
     if (t + 2 < n_kt) load_rows(kbase, t + 2, kreg);
     load_vpairs(t);
-    const bool next_active = t + 1 < n_kt && (t + 1) * kKT <= t_base + kQT - 1;
+    const bool next_active = t + 1 < n_kt && (t + 1) * kKT <= a_wave;
     if (next_active) qk(kslot((t + 1) & 1), snext);
-    if (t > 0 && (t - 1) * kKT <= t_base + kQT - 1) pv(pprev, vslot((t + 1) & 1));
-    if (t * kKT <= t_base + kQT - 1) {
+    if (t > 0 && (t - 1) * kKT <= a_wave) pv(pprev, vslot((t + 1) & 1));
+    if (t * kKT <= a_wave) {
       softmax(scur, t * kKT, true, pprev, alpha_prev, rescale_prev);
     } else {
       rescale_prev = false;
@@ -369,12 +375,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   }
   // the last tile's weighted sum
   if (rescale_prev) rescale_acc(alpha_prev);
-  if ((n_kt - 1) * kKT <= t_base + kQT - 1) pv(pprev, vslot((n_kt - 1) & 1));
+  if ((n_kt - 1) * kKT <= a_wave) pv(pprev, vslot((n_kt - 1) & 1));
 
   const float l = lrun + shfl_xor(lrun, 32);
   if (t_row < p.T) {
     const float inv = 1.f / l;
-    uint16_t* orow = p.out + ((int64_t(b) * p.T + t_row) * p.H + head) * D;
+    uint16_t* orow = p.out + ((int64_t(b) * p.T + t_row) * p.hm.o_heads + p.hm.o_head(g, qr)) * D;
 #pragma unroll
     for (int cb = 0; cb < C::kColBlocks; ++cb)
 #pragma unroll

@@ -95,25 +95,27 @@ __global__ __launch_bounds__(256) void rows_valu_kernel(RowsProblem p) {
 
   int len;
   if (p.causal) {
-    len = z % p.rows_per_batch + 1;
+    const int ctx = p.ctx_lens ? max(p.ctx_lens[b], 0) : 0;
+    len = min(ctx + z % p.rows_per_batch + 1, p.n_max);
   } else {
     len = p.seqlens[b];
     len = len < 0 ? 0 : (len > p.n_max ? p.n_max : len);
   }
   const int j0 = s * p.split_len;
   const int j1 = min(len, j0 + p.split_len);
-  const int h0 = g * p.n_rep + hb * kHeadsPerBlock;
-  const int nh = min(kHeadsPerBlock, p.n_rep - hb * kHeadsPerBlock);
+  const int r0 = hb * kHeadsPerBlock;             // first query of the group in this block
+  const int h0 = g * p.n_rep + r0;
+  const int nh = min(kHeadsPerBlock, p.n_rep - r0);
 
   // Query chunk of every head, pre-multiplied by scale*log2(e) so that the
   // scores come out in base-2 units.
   const float qmul = p.scale * kLog2e;
   float qf[kHeadsPerBlock][EPL];
-  const char* qrow = static_cast<const char*>(p.q) + (int64_t(z) * p.q_row_stride) * E::kSize;
+  const char* qrow = static_cast<const char*>(p.q) + (int64_t(z) * p.hm.q_heads * D) * E::kSize;
 #pragma unroll
   for (int hh = 0; hh < kHeadsPerBlock; ++hh) {
     if (hh < nh) {
-      E::load16(qrow + (int64_t(h0 + hh) * D + c * EPL) * E::kSize, qf[hh]);
+      E::load16(qrow + (p.hm.q_head(g, r0 + hh) * D + c * EPL) * E::kSize, qf[hh]);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) qf[hh][e] *= qmul;
     } else {
@@ -215,7 +217,8 @@ __global__ __launch_bounds__(256) void rows_valu_kernel(RowsProblem p) {
     }
     const int h = h0 + hh;
     if (p.num_splits == 1) {
-      char* orow = static_cast<char*>(p.out) + (int64_t(z) * p.q_row_stride + int64_t(h) * D) * E::kSize;
+      char* orow = static_cast<char*>(p.out) +
+                   ((int64_t(z) * p.hm.o_heads + p.hm.o_head(g, r0 + hh)) * D) * E::kSize;
       E::store(orow, col, L > 0.f ? O / L : 0.f);
     } else {
       const int64_t pr = (int64_t(z) * p.H + h) * p.num_splits + s;

@@ -192,6 +192,62 @@ gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void*
                               void* stream);
 
 /*
+ * gqa_prefill_chunk - a chunk of a prompt attending the cache it extends
+ * (chunked prefill).
+ *
+ * The prompt phase's causal rule -- each position sees itself and every
+ * earlier position (the blog's decoder discussion; gqa_prefill_causal) -- for
+ * T new positions that follow ctx_lens[b] positions already in the cache.  As
+ * in gqa_decode, the chunk's own K/V are already written, at cache positions
+ * ctx_lens[b] .. ctx_lens[b] + T - 1:
+ *
+ *   out[b,t,h,:] = sum_{j <= a} softmax_j(scale * q[b,t,h,:] . K[b,g,j,:]) V[b,g,j,:]
+ *   with g = floor(h * G / H), a = min(ctx_lens[b] + t, n_max - 1).
+ *
+ *   q        [B, T, H, d]       dtype, device
+ *   k_cache  [B, G, n_max, d]   dtype, device (the gqa_decode layout)
+ *   v_cache  [B, G, n_max, d]
+ *   ctx_lens [B] int32, device: cached positions before the chunk (negative
+ *            reads as 0).  Rows whose position would pass the cache are
+ *            clamped to the last slot.  Positions after a row's own are
+ *            never read into its arithmetic.
+ *   out      [B, T, H, d]       dtype, device; written in full.
+ *   n_max >= 1.  T = 1 is a decode step with seqlens = ctx_lens + 1; ctx = 0
+ *   with the prompt in the cache is gqa_prefill_causal.  Errors as for
+ *   gqa_prefill_causal (ctx_lens NULL is GQA_ERR_INVALID_ARG).
+ */
+gqa_status gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* ctx_lens, void* out,
+                             int B, int T, int H, int G, int d, int n_max, float scale, int dtype,
+                             void* stream);
+
+/*
+ * GQKVA - grouped queries AND grouped keys/values (the GQKVA summary on
+ * hub.baai.ac.cn): g_q query projections and g_kv key/value projections, one
+ * attention for every (query group i, K/V group j) pair, g_q * g_kv outputs.
+ * Output head h pairs query group i = h / g_kv with K/V group j = h % g_kv
+ * (query-group-major; the pages do not fix the order).  g_q = 1 is MKVA.
+ *
+ * gqkva_decode: q [B, g_q, d]; k_cache, v_cache [B, g_kv, n_max, d];
+ *   seqlens as in gqa_decode; out [B, g_q * g_kv, d]:
+ *   out[b,h,:] = sum_{j < n_b} softmax_j(scale * q[b,i,:] . K[b,j',j,:]) V[b,j',j,:]
+ *   with (i, j') the pair of h.  Each K/V row is read once for all g_q
+ *   queries.  Workspace: gqkva_decode_workspace_bytes() (same contract as
+ *   gqa_decode's); num_splits as in gqa_decode_split.
+ * gqkva_prefill_causal: q [B, T, g_q, d]; k, v [B, T, g_kv, d];
+ *   out [B, T, g_q * g_kv, d]; position t attends keys 0..t.
+ * Errors as for gqa_decode / gqa_prefill_causal (g_q, g_kv >= 1; any ratio).
+ */
+gqa_status gqkva_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seqlens, void* out,
+                        int B, int g_q, int g_kv, int d, int n_max, float scale, int dtype,
+                        int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+size_t gqkva_decode_workspace_bytes(int B, int g_q, int g_kv, int d, int n_max, int num_splits);
+gqa_status gqkva_prefill_causal(const void* q, const void* k, const void* v, void* out,
+                                int B, int T, int g_q, int g_kv, int d, float scale, int dtype,
+                                void* stream);
+
+/*
  * kv_meanpool_heads - MHA -> GQA checkpoint conversion of one projection.
  *
  * GQA paper section 2.1 (Figure 1) and section 2.2; tutorial section 4.3,

@@ -35,7 +35,8 @@ def lib():
 def test_header_declares_the_api():
     names = declared_functions()
     for n in ("gqa_decode", "gqa_decode_split", "gqa_decode_append", "gqa_prefill_causal",
-              "kv_meanpool_heads",
+              "gqa_prefill_chunk", "gqkva_decode", "gqkva_decode_workspace_bytes",
+              "gqkva_prefill_causal", "kv_meanpool_heads",
               "gqa_decode_workspace_bytes", "gqa_decode_num_splits", "gqa_status_string",
               "gqa_last_error", "gqa_version"):
         assert n in names, n
@@ -181,3 +182,41 @@ def test_decode_append_rejects_bad_arguments(lib):
     assert _append(lib, B=16, H=32, G=8, d=128, n=1024) == WORKSPACE
     # B = 0: nothing to do, no pointer looked at
     assert _append(lib, q=z, kn=z, vn=z, k=z, v=z, sl=z, out=z, B=0) == OK
+
+
+def _chunk(lib, q=P, k=P, v=P, ctx=P, out=P, B=2, T=16, H=8, G=2, d=64, n=128, scale=0.125, dt=BF16):
+    return lib.gqa_prefill_chunk(q, k, v, ctx, out, B, T, H, G, d, n, scale, dt, None)
+
+
+def test_prefill_chunk_rejects_bad_arguments(lib):
+    z = ctypes.c_void_p(0)
+    assert _chunk(lib, ctx=z) == INVALID
+    assert _chunk(lib, n=0) == INVALID
+    assert _chunk(lib, H=6, G=4) == INVALID
+    assert _chunk(lib, k=P_MIS) == INVALID
+    assert _chunk(lib, dt=9) == INVALID
+    assert _chunk(lib, scale=float("nan")) == INVALID
+    assert _chunk(lib, d=80) == UNSUPPORTED
+    assert _chunk(lib, q=z, k=z, v=z, ctx=z, out=z, B=0) == OK
+    assert _chunk(lib, q=z, k=z, v=z, ctx=z, out=z, T=0) == OK
+
+
+def test_gqkva_arguments_and_workspace(lib):
+    z = ctypes.c_void_p(0)
+    def dec(**kw):
+        a = dict(q=P, k=P, v=P, sl=P, out=P, B=2, gq=3, gkv=2, d=64, n=128, scale=0.1, dt=BF16, S=0)
+        a.update(kw)
+        return lib.gqkva_decode(a["q"], a["k"], a["v"], a["sl"], a["out"], a["B"], a["gq"], a["gkv"], a["d"],
+                                a["n"], a["scale"], a["dt"], a["S"], z, 0, None)
+    assert dec(gkv=0) == INVALID
+    assert dec(gq=0) == INVALID
+    assert dec(d=96) == UNSUPPORTED
+    assert dec(q=z, k=z, v=z, sl=z, out=z, B=0) == OK
+    # a ratio that is not a whole number is fine for GQKVA: only the workspace is missing here
+    assert dec(B=16, gq=3, gkv=8, d=128, n=1024) == WORKSPACE
+    need = lib.gqkva_decode_workspace_bytes(16, 3, 8, 128, 1024, 0)
+    S = lib.gqa_decode_num_splits(16, 8, 8, 128, 1024)          # same plan as G = 8 K/V heads
+    assert need == 65536 + (16 * 24 * S * 128 * 4 + 255) // 256 * 256 + 16 * 24 * S * 2 * 4
+    assert lib.gqkva_decode_workspace_bytes(16, 3, 0, 128, 1024, 0) == ctypes.c_size_t(-1).value
+    assert lib.gqkva_prefill_causal(z, z, z, z, 0, 16, 2, 3, 64, 0.1, BF16, None) == OK
+    assert lib.gqkva_prefill_causal(P, P, P, P, 1, 16, 2, 0, 64, 0.1, BF16, None) == INVALID
