@@ -166,6 +166,49 @@ def bench_prefill(torch, gqa, synth, steps, warmup, dtype=None):
             "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1)}
 
 
+def bench_prefill_chunk(torch, gqa, synth, steps, warmup, ctx=2048, T=2048):
+    """A T-token prompt chunk after ctx cached tokens (Llama-7B-sized layer, bf16)."""
+    B, H, G, d = 2, 32, 8, 128
+    n_max = ctx + T
+    dev = "cuda:0"
+    x = synth.decode_inputs(B, H, G, d, n_max, dtype="bf16", seed=21, device=dev)
+    q = synth.prefill_inputs(B, T, H, G, d, dtype="bf16", seed=22, device=dev)["q"]
+    cl = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    scale = synth.scale_for(d)
+    ms = _time_calls(torch, lambda i: gqa.prefill_chunk(q, x["k_cache"], x["v_cache"], cl, scale=scale,
+                                                        out=out), steps, warmup)
+    attended = B * H * (T * ctx + T * (T + 1) // 2)      # (row, key) pairs
+    fl = 4 * d * attended
+    tf = fl / (ms * 1e-3) / 1e12
+    del x, q, out
+    torch.cuda.empty_cache()
+    return {"B": B, "T": T, "ctx": ctx, "H": H, "G": G, "d": d, "dtype": "bf16",
+            "ms_per_call": round(ms, 6), "flops_per_call": fl, "TFLOPs": round(tf, 1),
+            "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+
+def bench_gqkva_decode(torch, gqa, synth, steps, warmup, g_q=4, g_kv=8):
+    """GQKVA decode on the Llama-7B-sized cache: g_q query groups x g_kv K/V groups."""
+    B, d, N = 16, 128, 1024
+    dev = "cuda:0"
+    kv_bytes = 2 * B * g_kv * N * d * 2
+    R = max(1, min(64, math.ceil((1 << 30) / kv_bytes)))
+    reps = [synth.decode_inputs(B, g_q, g_kv, d, N, dtype="bf16", seed=30 + r, device=dev) for r in range(R)]
+    out = torch.empty((B, g_q * g_kv, d), dtype=torch.bfloat16, device=dev)
+    scale = synth.scale_for(d)
+    ms = _time_calls(torch, lambda i: gqa.gqkva_decode(reps[i % R]["q"], reps[i % R]["k_cache"],
+                                                       reps[i % R]["v_cache"], reps[i % R]["seqlens"],
+                                                       scale=scale, out=out), steps, warmup)
+    nbytes = 2 * B * g_kv * N * d * 2 + B * g_q * d * 2 + B * g_q * g_kv * d * 2 + 4 * B
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    del reps
+    torch.cuda.empty_cache()
+    return {"B": B, "g_q": g_q, "g_kv": g_kv, "d": d, "N": N, "dtype": "bf16", "replicas": R,
+            "ms_per_call": round(ms, 6), "bytes_per_call": nbytes, "GBps": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def bench_meanpool(torch, gqa, synth, steps, warmup):
     w = synth.WORKLOADS["t5xxl_meanpool_bf16"]
     per_head = 1
@@ -289,6 +332,9 @@ def main():
         secondary["causal_prefill"] = bench_prefill(torch, gqa, synth, max(20, args.steps // 5), 3)
         secondary["causal_prefill_f16"] = bench_prefill(torch, gqa, synth, max(20, args.steps // 5), 3,
                                                         dtype="f16")
+        secondary["prefill_chunk_2048_after_2048"] = bench_prefill_chunk(torch, gqa, synth,
+                                                                         max(20, args.steps // 5), 3)
+        secondary["gqkva_decode_q4_kv8"] = bench_gqkva_decode(torch, gqa, synth, args.steps, args.warmup)
         secondary["t5xxl_meanpool"] = bench_meanpool(torch, gqa, synth, args.steps, args.warmup)
         secondary["hbm_copy_probe"] = bench_copy_probe(torch, args.steps)
         secondary["hbm_read_probe"] = bench_read_probe(torch, args.steps)
