@@ -260,7 +260,7 @@ gqa_status prefill_impl(const char* name, const void* q, const void* k, const vo
   const int64_t kv_g = cache_layout ? int64_t(n_max) * d : d;
   const int64_t kv_p = cache_layout ? d : int64_t(G) * d;
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
-  if (dtype != GQA_DTYPE_F32 && gqa::prefill_mfma_supports(n_rep, d)) {
+  if (dtype != GQA_DTYPE_F32 && gqa::prefill_mfma_supports(n_rep, d, kv_cap, kv_p)) {
     gqa::PrefillProblem p{};
     p.q = static_cast<const uint16_t*>(q);
     p.k = static_cast<const uint16_t*>(k);

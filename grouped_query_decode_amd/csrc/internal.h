@@ -125,7 +125,7 @@ bool decode_mfma_supports(int n_rep, int d, int num_splits, int split_len);
 hipError_t launch_combine(const CombineProblem& p, hipStream_t stream);
 hipError_t launch_append(const AppendProblem& p, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillProblem& p, hipStream_t stream);
-bool prefill_mfma_supports(int n_rep, int d);
+bool prefill_mfma_supports(int n_rep, int d, int kv_cap, int64_t kv_pstride);
 hipError_t launch_meanpool(const MeanpoolProblem& p, hipStream_t stream);
 
 }  // namespace gqa

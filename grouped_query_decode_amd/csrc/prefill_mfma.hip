@@ -167,20 +167,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   const int kl0 = tid / C::kChunks;
   const int ch0 = tid % C::kChunks;
   constexpr int kRowStep = kThreads / C::kChunks;
-  auto load_rows = [&](const uint16_t* base, int kt, u32x4_t* reg) {
-    const int key0 = kt * kKT + kl0;
-    const uint16_t* ptr = base + int64_t(key0) * kv_row + ch0 * 8;
-    if (kt * kKT + kKT <= kv_end) {                // whole tile seen by some row here
+  // Positions [0, kv_end) of this (b, g) through buffer resources that end
+  // there: loads past the end return zeros without a memory access, so the
+  // tile loads need no per-lane branches.  (The host keeps every offset below
+  // 2^31.)
+  const int row_bytes = int(kv_row) * 2;
+  const uint32_t kv_bytes = uint32_t((kv_end - 1) * row_bytes + D * 2);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kbase), 0, kv_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vbase), 0, kv_bytes, 0x00020000);
+  auto load_rows = [&](int kt, u32x4_t* reg) {
+    const int off0 = (kt * kKT + kl0) * row_bytes + ch0 * 16;
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) reg[i] = ld16(ptr + int64_t(i * kRowStep) * kv_row);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i) {
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (key0 + i * kRowStep < kv_end) w = ld16(ptr + int64_t(i * kRowStep) * kv_row);
-        reg[i] = w;
-      }
-    }
+    for (int i = 0; i < kLoads; ++i)
+      reg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off0 + i * kRowStep * row_bytes, 0, 0);
   };
   // V tiles: each thread loads key pairs (2p, 2p+1) x one 16-byte chunk; a
   // wave's lanes cover 32 pairs x 2 chunks (so that its transposed writes
@@ -194,12 +195,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
       const int item = tid + j * kThreads;
       const int pr = item & 31;
       const int ch = 2 * (item >> 6) + ((item >> 5) & 1);
-      const int key = kt * kKT + 2 * pr;
+      const int off = (kt * kKT + 2 * pr) * row_bytes + ch * 16;
       u32x4_t w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
-      if (item < kVPairItems) {
-        const uint16_t* ptr = vbase + int64_t(key) * kv_row + ch * 8;
-        if (key < kv_end) w0 = ld16(ptr);
-        if (key + 1 < kv_end) w1 = ld16(ptr + kv_row);
+      if (item < kVPairItems) {              // uniform per wave
+        w0 = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+        w1 = __builtin_amdgcn_raw_buffer_load_b128(rv, off + row_bytes, 0, 0);
       }
       vpr[j][0] = w0;
       vpr[j][1] = w1;
@@ -236,17 +236,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   // scores of one tile: lane holds S^T[key0 + 32*kb + 8*(r/4) + 4*h2 + r%4][t_row];
   // two independent accumulator chains (key blocks kb = 0, 1) interleaved
   auto qk = [&](const char* sk, f32x16_t* sc) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
     const char* krow0 = sk + l32 * C::kKPitch + h2 * 16;
+    const f32x16_t zero = {};
 #pragma unroll
     for (int ks = 0; ks < C::kSteps; ++ks) {
       const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(krow0 + ks * 32);
       const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(krow0 + 32 * C::kKPitch + ks * 32);
-      sc[0] = mfma32<DT>(k0, qop[ks], sc[0]);
-      sc[1] = mfma32<DT>(k1, qop[ks], sc[1]);
+      sc[0] = mfma32<DT>(k0, qop[ks], ks == 0 ? zero : sc[0]);
+      sc[1] = mfma32<DT>(k1, qop[ks], ks == 0 ? zero : sc[1]);
     }
   };
 
@@ -322,56 +319,74 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   // freed.  Tiles before t_split lie wholly below every row of the workgroup
   // (no mask) and have a successor; the rest take the masked path.
   const int t_split = min(n_kt - 1, min(ctx + qt * rows_wg, last_pos) / kKT);
-  load_rows(kbase, 0, kreg);
+  load_rows(0, kreg);
   store_rows(kslot(0), C::kKPitch, kreg);
   if (n_kt > 1) {
-    load_rows(kbase, 1, kreg);
+    load_rows(1, kreg);
     store_rows(kslot(1), C::kKPitch, kreg);
   }
   __syncthreads();
-  f32x16_t scur[2], snext[2];
-  qk(kslot(0), scur);
+  // Two score buffers alternate between "this tile" and "next tile" (the
+  // loops below are unrolled by two), so no copy sits between a tile's score
+  // MFMAs and its softmax.
+  f32x16_t sa[2], sb[2];
+  qk(kslot(0), sa);
+  // every wave has read K(0) before the first iteration overwrites its slot
+  __syncthreads();
   u32x4_t pprev[4];
   float alpha_prev = 1.f;
   bool rescale_prev = false;
 
   // one unmasked iteration (with_pv is a constant at each call site, so the
-  // region below has no branch)
-  auto iter_unmasked = [&](int t, bool with_pv) {
+  // region below has no branch); cur holds tile t's scores, nxt receives t+1's
+  auto iter_unmasked = [&](int t, bool with_pv, f32x16_t* cur, f32x16_t* nxt) {
     if (rescale_prev) rescale_acc(alpha_prev);
-    load_rows(kbase, min(t + 2, n_kt - 1), kreg);
+    load_rows(min(t + 2, n_kt - 1), kreg);
     load_vpairs(t);
-    qk(kslot((t + 1) & 1), snext);
+    qk(kslot((t + 1) & 1), nxt);
     if (with_pv) pv(pprev, vslot((t + 1) & 1));
-    softmax(scur, t * kKT, false, pprev, alpha_prev, rescale_prev);
+    softmax(cur, t * kKT, false, pprev, alpha_prev, rescale_prev);
     store_rows(kslot(t & 1), C::kKPitch, kreg);    // K(t) was read by the scores of tile t
     store_vt(vslot(t & 1));                        // V(t-2) was summed at iteration t-1
     __syncthreads();
-    scur[0] = snext[0];
-    scur[1] = snext[1];
   };
-  int t = 0;
-  if (t_split > 0) {
-    iter_unmasked(0, false);
-    for (t = 1; t < t_split; ++t) iter_unmasked(t, true);
-  }
-  for (; t < n_kt; ++t) {                          // tiles that reach the diagonal
+  // one iteration on a tile that may reach the diagonal
+  auto iter_masked = [&](int t, f32x16_t* cur, f32x16_t* nxt) {
     if (rescale_prev) rescale_acc(alpha_prev);
-    if (t + 2 < n_kt) load_rows(kbase, t + 2, kreg);
+    if (t + 2 < n_kt) load_rows(t + 2, kreg);
     load_vpairs(t);
     const bool next_active = t + 1 < n_kt && (t + 1) * kKT <= a_wave;
-    if (next_active) qk(kslot((t + 1) & 1), snext);
+    if (next_active) qk(kslot((t + 1) & 1), nxt);
     if (t > 0 && (t - 1) * kKT <= a_wave) pv(pprev, vslot((t + 1) & 1));
     if (t * kKT <= a_wave) {
-      softmax(scur, t * kKT, true, pprev, alpha_prev, rescale_prev);
+      softmax(cur, t * kKT, true, pprev, alpha_prev, rescale_prev);
     } else {
       rescale_prev = false;
     }
     if (t + 2 < n_kt) store_rows(kslot(t & 1), C::kKPitch, kreg);
     store_vt(vslot(t & 1));
     __syncthreads();
-    scur[0] = snext[0];
-    scur[1] = snext[1];
+  };
+  // tile t's scores are in sa for even t, in sb for odd t
+  int t = 0;
+  if (t_split > 0) {
+    iter_unmasked(0, false, sa, sb);
+    for (t = 1; t + 1 < t_split; t += 2) {
+      iter_unmasked(t, true, sb, sa);
+      iter_unmasked(t + 1, true, sa, sb);
+    }
+    if (t < t_split) {
+      iter_unmasked(t, true, sb, sa);
+      ++t;
+    }
+  }
+  if (t < n_kt && (t & 1)) {
+    iter_masked(t, sb, sa);
+    ++t;
+  }
+  for (; t < n_kt; t += 2) {                       // tiles that reach the diagonal
+    iter_masked(t, sa, sb);
+    if (t + 1 < n_kt) iter_masked(t + 1, sb, sa);
   }
   // the last tile's weighted sum
   if (rescale_prev) rescale_acc(alpha_prev);
@@ -395,8 +410,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
 
 }  // namespace
 
-bool prefill_mfma_supports(int n_rep, int d) {
-  return (d == 64 || d == 128) && (n_rep == 1 || n_rep == 2 || n_rep % 4 == 0);
+bool prefill_mfma_supports(int n_rep, int d, int kv_cap, int64_t kv_pstride) {
+  // byte offsets of the K/V buffer loads (up to a tile past the end) stay below 2^31
+  const int64_t reach = (int64_t(kv_cap) + 2 * kKT) * kv_pstride * 2;
+  return (d == 64 || d == 128) && (n_rep == 1 || n_rep == 2 || n_rep % 4 == 0) &&
+         reach < (int64_t(1) << 31);
 }
 
 hipError_t launch_prefill_mfma(const PrefillProblem& p, hipStream_t stream) {
