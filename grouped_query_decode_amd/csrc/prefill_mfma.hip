@@ -27,8 +27,11 @@
 // the vector unit independent work.  Softmax work per score: one FMA
 // (scale folded in), one hardware exp2 (weights below 2^-126 may flush to
 // zero), a third of a max3, half a 16-bit pack, half a
-// 16-bit dot2 for the normaliser (which sums the rounded weights); the running
-// output is rescaled only when some row's maximum grew.  Query tiles are issued
+// 16-bit dot2 for the normaliser (which sums the rounded weights).  The
+// reference maximum a row's weights are taken against moves only when a tile
+// raises the row's maximum by more than kLazyLog2 (base 2): weights then stay
+// below 2^kLazyLog2 and the running output is rescaled rarely (after the first
+// tiles, almost never on data of moderate range).  Query tiles are issued
 // heaviest first, and the query tiles of a (b, g) stay on one XCD (consecutive
 // workgroups go to consecutive XCDs) so its K/V stays in that XCD's L2.
 
@@ -41,6 +44,9 @@ namespace {
 constexpr int kKT = 64;     // keys per tile
 constexpr int kQT = 32;     // query positions per wave
 constexpr int kXcds = 8;
+// Largest base-2 growth of a row maximum absorbed without rescaling (weights
+// up to 2^8 are exact enough in 16 bits and harmless in float32 sums).
+constexpr float kLazyLog2 = 8.f;
 
 
 // LDS tiles (64 banks of 4 bytes):
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
       const int ch = 2 * (item >> 6) + ((item >> 5) & 1);
       const int off = (kt * kKT + 2 * pr) * row_bytes + ch * 16;
       u32x4_t w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
-      if (item < kVPairItems) {              // uniform per wave
+      if (kVItems * kThreads == kVPairItems || item < kVPairItems) {   // uniform per wave
         w0 = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
         w1 = __builtin_amdgcn_raw_buffer_load_b128(rv, off + row_bytes, 0, 0);
       }
@@ -209,7 +215,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
 #pragma unroll
     for (int j = 0; j < kVItems; ++j) {
       const int item = tid + j * kThreads;
-      if (item < kVPairItems) {
+      if (kVItems * kThreads == kVPairItems || item < kVPairItems) {
         const int pr = item & 31;
         const int ch = 2 * (item >> 6) + ((item >> 5) & 1);
         char* col = dst + (8 * ch) * C::kVtPitch + vt_pos(2 * pr) * 2;
@@ -266,8 +272,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) tmax = fmaxf(fmaxf(tmax, sc[kb][r]), sc[kb][r + 1]);
-    const float mn = fmaxf(tmax, shfl_xor(tmax, 32));   // finite: key 0 precedes every row
-    const float mc = mn * c2;
+    // row maximum over both lane halves (one register swap, no LDS round trip);
+    // finite: key 0 precedes every row
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
+                                                     false, false);
+    const float mn = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    const bool grow = __any(mrun == -INFINITY || (mn - mrun) * c2 > kLazyLog2);
+    const float mref = grow ? mn : mrun;            // wave-uniform choice
+    const float mc = mref * c2;
     float lsum = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -282,10 +294,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
       }
       pop[u] = u32x4_t{w[0], w[1], w[2], w[3]};
     }
-    alpha = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun * c2 - mc);
-    rescale = __any(mn != mrun);                   // some row's maximum grew
+    alpha = grow ? (mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun * c2 - mc)) : 1.f;
+    rescale = grow;
     lrun = fmaf(lrun, alpha, lsum);
-    mrun = mn;
+    mrun = mref;
   };
 
   // O^T += V^T P^T: A = V^T[32*cb + l32][keys of k-step u, half h2], one
@@ -304,6 +316,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
     }
   };
   auto rescale_acc = [&](float alpha) {
+    asm volatile("");       // keeps the (rare) rescale a branch rather than a multiply by 1
 #pragma unroll
     for (int cb = 0; cb < C::kColBlocks; ++cb) acc[cb] *= alpha;
   };
@@ -312,18 +325,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   // region with no branch inside: the score MFMAs of tile t+1, the weighted
   // sum of tile t-1 (its weights were made one iteration earlier) and the
   // softmax of tile t -- independent work for the matrix and the vector unit
-  // of the same wave.  The running output is rescaled (rarely: only when a
-  // row's maximum grew) at the top of the iteration, before tile t-1's weights
-  // are added.  LDS: K slot (t+1)&1 holds K(t+1), V slot (t+1)&1 holds V(t-1);
+  // of the same wave.  When tile t moved a row's reference maximum (rare),
+  // the running output -- which by then holds the tiles up to t-1 -- is
+  // rescaled at the end of the iteration, before tile t's weights are added
+  // at the next one.  LDS: K slot (t+1)&1 holds K(t+1), V slot (t+1)&1 holds V(t-1);
   // the global loads of K(t+2) and V(t) land in the slots t&1 this iteration
   // freed.  Tiles before t_split lie wholly below every row of the workgroup
   // (no mask) and have a successor; the rest take the masked path.
   const int t_split = min(n_kt - 1, min(ctx + qt * rows_wg, last_pos) / kKT);
-  load_rows(0, kreg);
-  store_rows(kslot(0), C::kKPitch, kreg);
-  if (n_kt > 1) {
-    load_rows(1, kreg);
-    store_rows(kslot(1), C::kKPitch, kreg);
+  {
+    // both first K tiles in flight at once (tile 1 reads as zeros past the end)
+    u32x4_t kreg1[kLoads];
+    load_rows(0, kreg);
+    load_rows(1, kreg1);
+    store_rows(kslot(0), C::kKPitch, kreg);
+    store_rows(kslot(1), C::kKPitch, kreg1);
   }
   __syncthreads();
   // Two score buffers alternate between "this tile" and "next tile" (the
@@ -340,7 +356,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   // one unmasked iteration (with_pv is a constant at each call site, so the
   // region below has no branch); cur holds tile t's scores, nxt receives t+1's
   auto iter_unmasked = [&](int t, bool with_pv, f32x16_t* cur, f32x16_t* nxt) {
-    if (rescale_prev) rescale_acc(alpha_prev);
     load_rows(min(t + 2, n_kt - 1), kreg);
     load_vpairs(t);
     qk(kslot((t + 1) & 1), nxt);
@@ -348,11 +363,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
     softmax(cur, t * kKT, false, pprev, alpha_prev, rescale_prev);
     store_rows(kslot(t & 1), C::kKPitch, kreg);    // K(t) was read by the scores of tile t
     store_vt(vslot(t & 1));                        // V(t-2) was summed at iteration t-1
+    // the weights are made here, ahead of the branch (not sunk into the next
+    // iteration, which would leave the matrix work above without vector work)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) asm volatile("" ::"v"(pprev[u]));
+    if (rescale_prev) rescale_acc(alpha_prev);
     __syncthreads();
   };
   // one iteration on a tile that may reach the diagonal
   auto iter_masked = [&](int t, f32x16_t* cur, f32x16_t* nxt) {
-    if (rescale_prev) rescale_acc(alpha_prev);
     if (t + 2 < n_kt) load_rows(t + 2, kreg);
     load_vpairs(t);
     const bool next_active = t + 1 < n_kt && (t + 1) * kKT <= a_wave;
@@ -365,6 +384,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
     }
     if (t + 2 < n_kt) store_rows(kslot(t & 1), C::kKPitch, kreg);
     store_vt(vslot(t & 1));
+    if (rescale_prev) rescale_acc(alpha_prev);
     __syncthreads();
   };
   // tile t's scores are in sa for even t, in sb for odd t
@@ -388,8 +408,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
     iter_masked(t, sa, sb);
     if (t + 1 < n_kt) iter_masked(t + 1, sb, sa);
   }
-  // the last tile's weighted sum
-  if (rescale_prev) rescale_acc(alpha_prev);
+  // the last tile's weighted sum (any rescale it needs was applied above)
   if ((n_kt - 1) * kKT <= a_wave) pv(pprev, vslot((n_kt - 1) & 1));
 
   const float l = lrun + shfl_xor(lrun, 32);
