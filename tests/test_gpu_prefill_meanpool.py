@@ -52,6 +52,76 @@ def test_prefill_cases(B, T, H, G, d, dt):
     assert torch.equal(out[:, 0], want0)
 
 
+def _ramp_inputs(B, T, H, G, d, dt, step_log2, seed, spike=None):
+    """Seeded prefill inputs whose scores drift by step_log2 (base 2) every 64 keys.
+
+    Dimension 0 of every query is a constant a and dimension 0 of key j grows
+    linearly with j, so scale*log2(e)*q.k[j] = step_log2*j/64 + noise: a
+    positive step raises each row's maximum tile after tile (above 8 per tile
+    the kernel must rescale its running output every tile), a negative one
+    keeps the maximum at key 0.  With spike=(position, jump) that key alone gets
+    an extra score of jump (base 2).
+    """
+    gen = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, T, H, d, generator=gen) * 0.5
+    k = torch.randn(B, T, G, d, generator=gen) * 0.5
+    v = torch.randn(B, T, G, d, generator=gen)
+    a = 4.0
+    c = synth.scale_for(d) * 1.4426950408889634 * a          # base-2 score per unit of k[..., 0]
+    q[..., 0] = a
+    k[..., 0] = (step_log2 / 64.0) * torch.arange(T, dtype=torch.float32)[None, :, None] / c
+    if spike is not None:
+        pos, jump = spike
+        k[:, pos, :, 0] += jump / c
+    dtype = synth.torch_dtype(dt)
+    return {n: t.to(dtype).to(DEV) for n, t in (("q", q), ("k", k), ("v", v))}
+
+
+@pytest.mark.parametrize("step", [-12.0, 4.0, 9.0, 12.0])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_prefill_growing_row_maxima(step, dt):
+    """Row maxima that keep growing tile after tile (and one that never grows):
+    the running output is rescaled on exactly those tiles, and the result must
+    not depend on when that happens."""
+    announce(f"prefill ramp step={step} {dt}")
+    B, T, H, G, d = 1, 520, 8, 2, 128
+    x = _ramp_inputs(B, T, H, G, d, dt, step, seed=int(step * 10) + 7)
+    scale = synth.scale_for(d)
+    out = _prefill(x, scale)
+    ref = oracle.prefill_causal_ref(to64(x["q"]), to64(x["k"]), to64(x["v"]), scale)
+    assert_close(out, ref, x["q"].dtype, f"prefill ramp {step}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_prefill_late_score_spike(dt):
+    """One key far into the prompt outscores everything before it by 2^40:
+    rows at or after it must switch to it (their running output is rescaled by
+    about 2^-40), rows before it must not see it."""
+    announce(f"prefill late spike {dt}")
+    B, T, H, G, d = 2, 400, 8, 2, 128
+    x = _ramp_inputs(B, T, H, G, d, dt, 0.0, seed=11, spike=(301, 40.0))
+    scale = synth.scale_for(d)
+    out = _prefill(x, scale)
+    ref = oracle.prefill_causal_ref(to64(x["q"]), to64(x["k"]), to64(x["v"]), scale)
+    assert_close(out, ref, x["q"].dtype, "prefill spike")
+
+
+def test_prefill_chunk_growing_row_maxima():
+    """The chunked form (queries after a cached prefix) on growing maxima."""
+    announce("prefill_chunk ramp")
+    B, T, H, G, d, ctx = 1, 200, 8, 2, 128, 300
+    x = _ramp_inputs(B, ctx + T, H, G, d, "bf16", 10.0, seed=5)
+    scale = synth.scale_for(d)
+    kc = x["k"].transpose(1, 2).contiguous()                 # [B, G, Nmax, d] cache layout
+    vc = x["v"].transpose(1, 2).contiguous()
+    q = x["q"][:, ctx:].contiguous()
+    cl = torch.full((B,), ctx, dtype=torch.int32, device=DEV)
+    out = gqa.prefill_chunk(q, kc, vc, cl, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_chunk_ref(to64(q), to64(kc), to64(vc), cl.cpu().numpy(), scale)
+    assert_close(out, ref, q.dtype, "prefill_chunk ramp")
+
+
 def test_prefill_row_matches_decode():
     """Prefill row i equals a decode step over the first i+1 positions."""
     announce("prefill vs decode rows")
