@@ -166,7 +166,14 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
   }
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
 
-  if (dtype != GQA_DTYPE_F32 && gqa::decode_mfma_supports(n_rep, d, S, split_len)) {
+  // A group of more than 16 queries (one matrix-core tile of heads) runs as
+  // several work groups of 16 that read the same K/V head: twice the
+  // workgroups for n_rep = 32, each with a single tile of heads; the second
+  // read of a K/V slice mostly comes from the last-level cache.
+  int kv_div = 1;
+  if (!gqkva && n_rep > 16 && n_rep % 16 == 0 && int64_t(B) * G * (n_rep / 16) <= kMaxCountedUnits)
+    kv_div = n_rep / 16;
+  if (dtype != GQA_DTYPE_F32 && gqa::decode_mfma_supports(n_rep / kv_div, d, S, split_len)) {
     gqa::DecodeProblem p{};
     p.q = static_cast<const uint16_t*>(q);
     p.k = static_cast<const uint16_t*>(k);
@@ -176,12 +183,13 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
     p.part_o = part_o;
     p.part_ml = part_ml;
     // the split merge runs inside the decode kernel when the counters fit
-    p.counters = (S > 1 && int64_t(B) * G <= kMaxCountedUnits) ? counters : nullptr;
+    p.counters = (S > 1 && int64_t(B) * G * kv_div <= kMaxCountedUnits) ? counters : nullptr;
     p.k_new = static_cast<const uint16_t*>(k_new);
     p.v_new = static_cast<const uint16_t*>(v_new);
     p.dtype = dtype;
-    p.hm = hm;
-    p.B = B; p.H = Hp; p.G = G; p.n_rep = n_rep; p.d = d; p.n_max = n_max;
+    p.hm = kv_div > 1 ? gqa::gqa_head_map(G * kv_div, n_rep / kv_div) : hm;
+    p.B = B; p.H = Hp; p.G = G * kv_div; p.n_rep = n_rep / kv_div; p.d = d; p.n_max = n_max;
+    p.kv_div = kv_div;
     p.scale = scale;
     p.num_splits = S;
     p.split_len = split_len;

@@ -8,7 +8,9 @@
 // Work unit: one workgroup of 1, 2 or 4 waves per (sequence b, K/V head g,
 // split s).  The group's n_rep query heads are the 16 columns of the
 // matrix-core tiles (padded with zero queries), so every cached K/V row is read
-// from HBM once and used by all heads of its group:
+// from HBM once and used by all heads of its group (a group of 32 or more
+// queries may instead be run as work groups of 16 that read the same K/V
+// head, the repeat coming mostly from the last-level cache):
 //
 //   scores  S^T[key][head] = K[key][:] . Q[head][:]     16x16x32 16-bit MFMA,
 //           A = 16 keys x 32 dims straight from HBM (16-byte loads),
@@ -177,8 +179,10 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   const int units = p.B * p.G;
   const int s = int(blockIdx.x / unsigned(units));
   const int unit = int(blockIdx.x % unsigned(units));
-  const int g = unit % p.G;
+  const int g = unit % p.G;                // work group: its n_rep queries
   const int b = unit / p.G;
+  const int g_kv = g / p.kv_div;           // the K/V head they read
+  const int G_kv = p.G / p.kv_div;
 
   const int raw_len = p.seqlens[b];
   const int len = raw_len < 0 ? 0 : (raw_len > p.n_max ? p.n_max : raw_len);
@@ -191,23 +195,24 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   const int j0 = s * p.split_len;
   const int j1 = min(len, j0 + p.split_len);
 
-  const int64_t kv_off = (int64_t(b) * p.G + g) * int64_t(p.n_max) * D;
+  const int64_t kv_off = (int64_t(b) * G_kv + g_kv) * int64_t(p.n_max) * D;
   const uint16_t* kb = p.k + kv_off;
   const uint16_t* vb = p.v + kv_off;
 
   // Append (when k_new is given): the new token's k, v belong in slot
   // raw_len-1 if that slot exists.  The split holding that slot writes them
-  // to the cache and attends them straight from a copy in LDS (no other
-  // workgroup reads that slot in this launch); its stream of cached rows
-  // stops just before the slot.
+  // to the cache (the first work group of the K/V head, when several share
+  // it) and attends them straight from a copy in LDS (no workgroup reads that
+  // slot from the cache in this launch); its stream of cached rows stops just
+  // before the slot.
   __shared__ __attribute__((aligned(16))) char s_new[2 * D * 2];
   const int p_new = (p.k_new != nullptr && raw_len >= 1 && raw_len <= p.n_max) ? raw_len - 1 : -1;
   const bool owner = p_new >= j0 && p_new < j1;
   if (owner && threadIdx.x < 2 * C::kChunks) {
     const int c = threadIdx.x % C::kChunks;
     const bool is_v = threadIdx.x >= C::kChunks;
-    const u32x4_t w = ld16((is_v ? p.v_new : p.k_new) + (int64_t(b) * p.G + g) * D + c * 8);
-    st16(const_cast<uint16_t*>(is_v ? vb : kb) + int64_t(p_new) * D + c * 8, w);
+    const u32x4_t w = ld16((is_v ? p.v_new : p.k_new) + (int64_t(b) * G_kv + g_kv) * D + c * 8);
+    if (g % p.kv_div == 0) st16(const_cast<uint16_t*>(is_v ? vb : kb) + int64_t(p_new) * D + c * 8, w);
     *reinterpret_cast<u32x4_t*>(s_new + (is_v ? D * 2 : 0) + c * 16) = w;
   }
 

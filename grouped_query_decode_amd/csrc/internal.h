@@ -65,7 +65,11 @@ struct DecodeProblem {
   const uint16_t* v_new;
   int dtype;                // kBF16 or kF16
   HeadMap hm;
+  // G work groups of n_rep queries; with kv_div > 1 a K/V head's queries are
+  // spread over kv_div consecutive work groups (blocks of n_rep), which all
+  // read that head: work group g reads K/V head g / kv_div of G / kv_div.
   int B, H, G, n_rep, d, n_max;   // H = G*n_rep (the partial results' layout)
+  int kv_div;
   float scale;
   int num_splits, split_len;
 };

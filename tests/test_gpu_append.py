@@ -61,6 +61,7 @@ CASES = [
     (3, 32, 8, 128, 777, "bf16", [777, 513, 256]),
     (2, 32, 32, 128, 129, "bf16", [129, 65]),
     (2, 32, 1, 128, 600, "bf16", [600, 257]),
+    (3, 64, 1, 64, 300, "bf16", [300, 1, 129]),          # four work groups share each K/V head
     (3, 64, 8, 64, 450, "bf16", [450, 1, 449]),
     (4, 24, 8, 128, 300, "bf16", [0, 301, 300, 2]),      # 0 and > Nmax write nothing
     (3, 8, 2, 64, 200, "f32", [200, 1, 77]),

@@ -80,7 +80,10 @@ CASES = [
     (2, 64, 8, 64, 450, "bf16"),
     (2, 16, 16, 64, 97, "bf16"),
     (2, 32, 2, 128, 160, "bf16"),
-    (2, 64, 2, 64, 130, "bf16"),      # n_rep = 32
+    (2, 64, 2, 64, 130, "bf16"),      # n_rep = 32: two work groups of 16 per K/V head
+    (2, 64, 1, 128, 333, "bf16"),     # n_rep = 64: four work groups of 16 per K/V head
+    (2, 48, 1, 64, 150, "f16"),       # n_rep = 48: three work groups of 16
+    (2, 40, 2, 128, 90, "bf16"),      # n_rep = 20: one work group, two tiles of heads
     (2, 24, 8, 128, 140, "bf16"),     # n_rep = 3
     (3, 8, 2, 128, 300, "f32"),
     (2, 32, 4, 64, 260, "f32"),
@@ -110,6 +113,16 @@ def test_forced_split_counts(dt, S):
                             seqlens=[1000, 513, 31], nan_tail=True)
     scale = synth.scale_for(128)
     assert_close(_run(x, scale, num_splits=S), _oracle(x, scale), x["q"].dtype, f"S={S}")
+
+
+@pytest.mark.parametrize("S", [1, 3, 7, 64])
+def test_forced_split_counts_large_group(S):
+    """n_rep = 32 (run as two work groups of 16 per K/V head) with every split count."""
+    announce(f"decode n_rep=32 forced splits S={S}")
+    x = synth.decode_inputs(3, 32, 1, 128, 1000, dtype="bf16", seed=13, device=DEV,
+                            seqlens=[1000, 1, 517], nan_tail=True)
+    scale = synth.scale_for(128)
+    assert_close(_run(x, scale, num_splits=S), _oracle(x, scale), x["q"].dtype, f"n_rep=32 S={S}")
 
 
 def test_lengths_zero_and_beyond_capacity():
