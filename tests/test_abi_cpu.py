@@ -220,3 +220,49 @@ def test_gqkva_arguments_and_workspace(lib):
     assert lib.gqkva_decode_workspace_bytes(16, 3, 0, 128, 1024, 0) == ctypes.c_size_t(-1).value
     assert lib.gqkva_prefill_causal(z, z, z, z, 0, 16, 2, 3, 64, 0.1, BF16, None) == OK
     assert lib.gqkva_prefill_causal(P, P, P, P, 1, 16, 2, 0, 64, 0.1, BF16, None) == INVALID
+
+
+C_CONSUMER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "gqa.h"
+
+/* Host-only calls of the C ABI from plain C: planning, sizes and argument
+   errors all return before any GPU work. */
+int main(void) {
+  char buf[16] __attribute__((aligned(16)));
+  void* p = buf;
+  int32_t lens[2] __attribute__((aligned(16))) = {1, 1};
+  if (gqa_version() < 100) return 1;
+  if (strcmp(gqa_status_string(GQA_OK), "GQA_OK") != 0) return 2;
+  int s = gqa_decode_num_splits(16, 32, 8, 128, 1024);
+  size_t ws = gqa_decode_workspace_bytes(16, 32, 8, 128, 1024, 0);
+  if (s < 1 || (s > 1 && ws == 0)) return 3;
+  /* H not a multiple of G: rejected on the host */
+  gqa_status st = gqa_decode(p, p, p, lens, p, 2, 6, 4, 64, 16, 0.125f, GQA_DTYPE_BF16, NULL, 0, NULL);
+  if (st != GQA_ERR_INVALID_ARG || strlen(gqa_last_error()) == 0) return 4;
+  /* an empty batch is a successful no-op */
+  if (gqa_prefill_causal(p, p, p, p, 0, 16, 8, 2, 64, 0.125f, GQA_DTYPE_BF16, NULL) != GQA_OK) return 5;
+  printf("splits=%d workspace=%zu version=%d\n", s, ws, gqa_version());
+  return 0;
+}
+"""
+
+
+def test_plain_c_consumer(tmp_path, lib):
+    """The header is C (not only C++): a C99 program includes it, links
+    libgqa.so and makes host-side calls."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "consumer.c"
+    src.write_text(C_CONSUMER)
+    exe = tmp_path / "consumer"
+    libdir = os.path.dirname(gqa.library_path())
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                    "-o", str(exe), "-L", libdir, "-lgqa", f"-Wl,-rpath,{libdir}"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert "splits=" in r.stdout
