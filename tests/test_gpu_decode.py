@@ -293,3 +293,32 @@ def test_ragged_long_context_decode():
     assert_close(out[rows], ref, torch.bfloat16, "ragged long")
     del x
     torch.cuda.empty_cache()
+
+
+def _random_shapes(n, seed):
+    """A fixed list of shapes drawn once from a seeded generator: every
+    supported head size, group sizes from MQA to MHA, lengths from 0 to past
+    the capacity, all three dtypes."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for _ in range(n):
+        G = int(rng.choice([1, 2, 4, 8]))
+        n_rep = int(rng.choice([1, 2, 3, 4, 5, 8, 16, 32]))
+        d = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 5))
+        n_max = int(rng.integers(1, 700))
+        dt = str(rng.choice(["bf16", "f16", "f32"]))
+        lens = [int(rng.integers(-2, n_max + 3)) for _ in range(B)]
+        shapes.append((B, G * n_rep, G, d, n_max, dt, lens))
+    return shapes
+
+
+@pytest.mark.parametrize("case", _random_shapes(24, 2024))
+def test_decode_random_shapes(case):
+    B, H, G, d, n_max, dt, lens = case
+    announce(f"decode random B={B} H={H} G={G} d={d} Nmax={n_max} {dt} lens={lens}")
+    x = synth.decode_inputs(B, H, G, d, n_max, dtype=dt, seed=B + H + n_max, device=DEV,
+                            seqlens=lens, nan_tail=False)
+    scale = synth.scale_for(d)
+    out = _run(x, scale)
+    assert_close(out, _oracle(x, scale), x["q"].dtype, f"random {case}")
