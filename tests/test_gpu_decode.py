@@ -322,3 +322,17 @@ def test_decode_random_shapes(case):
     scale = synth.scale_for(d)
     out = _run(x, scale)
     assert_close(out, _oracle(x, scale), x["q"].dtype, f"random {case}")
+
+
+# float32 at scale 2: softmax arguments near 100 turn one float32 rounding of
+# a score into a ~1e-5 relative change of its weight, so the float32 bound
+# (set for scale 1/sqrt(d)) cannot hold there; bfloat16 covers that case
+@pytest.mark.parametrize("scale,dt", [(0.0, "bf16"), (-0.3, "bf16"), (2.0, "bf16"),
+                                      (0.0, "f32"), (-0.3, "f32")])
+def test_decode_unusual_scales(scale, dt):
+    """scale 0 gives the plain mean of the attended V rows; a negative scale
+    favours the least similar keys; a large one makes the softmax nearly hard
+    (scores spread over dozens of powers of two)."""
+    announce(f"decode scale={scale} {dt}")
+    x = synth.decode_inputs(2, 32, 8, 128, 600, dtype=dt, seed=17, device=DEV, seqlens=[600, 345])
+    assert_close(_run(x, scale), _oracle(x, scale), x["q"].dtype, f"scale={scale}")

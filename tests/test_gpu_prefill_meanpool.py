@@ -242,3 +242,18 @@ def test_prefill_random_shapes(case):
     out = _prefill(x, scale)
     ref = oracle.prefill_causal_ref(to64(x["q"]), to64(x["k"]), to64(x["v"]), scale)
     assert_close(out, ref, x["q"].dtype, f"prefill random {case}")
+
+
+# float32 at scale 2: softmax arguments near 100 turn one float32 rounding of
+# a score into a ~1e-5 relative change of its weight, so the float32 bound
+# (set for scale 1/sqrt(d)) cannot hold there; bfloat16 covers that case
+@pytest.mark.parametrize("scale,dt", [(0.0, "bf16"), (-0.3, "bf16"), (2.0, "bf16"),
+                                      (0.0, "f32"), (-0.3, "f32")])
+def test_prefill_unusual_scales(scale, dt):
+    """As for decode: the mean of the visible rows at scale 0, the least similar
+    keys favoured at a negative scale, a nearly hard softmax at scale 2."""
+    announce(f"prefill scale={scale} {dt}")
+    x = synth.prefill_inputs(1, 300, 8, 2, 128, dtype=dt, seed=19, device=DEV, std=1.0)
+    out = _prefill(x, scale)
+    ref = oracle.prefill_causal_ref(to64(x["q"]), to64(x["k"]), to64(x["v"]), scale)
+    assert_close(out, ref, x["q"].dtype, f"prefill scale={scale}")
