@@ -144,10 +144,15 @@ __device__ __forceinline__ void merge_item(const DecodeProblem& p, const UnitPar
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const float lu = __uint_as_float(ml[u][1]);
-      const float f = lu > 0.f ? __builtin_amdgcn_exp2f(__uint_as_float(ml[u][0]) - cm) : 0.f;
-      L = fmaf(lu, f, L);
-      Oa += f * __builtin_bit_cast(f32x4_t, oa[u]);
-      Ob += f * __builtin_bit_cast(f32x4_t, ob[u]);
+      // Slots of splits that did not run in this call (or saw nothing) hold
+      // stale bytes -- possibly inf or NaN -- so they are selected away, never
+      // multiplied by zero.
+      if (lu > 0.f) {
+        const float f = __builtin_amdgcn_exp2f(__uint_as_float(ml[u][0]) - cm);
+        L = fmaf(lu, f, L);
+        Oa += f * __builtin_bit_cast(f32x4_t, oa[u]);
+        Ob += f * __builtin_bit_cast(f32x4_t, ob[u]);
+      }
     }
     M = cm;
   }

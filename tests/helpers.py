@@ -34,7 +34,11 @@ def to64(t: torch.Tensor) -> np.ndarray:
 def assert_close(got: torch.Tensor, ref: np.ndarray, dtype: torch.dtype, what: str = "") -> dict:
     g = to64(got)
     assert g.shape == ref.shape, (g.shape, ref.shape)
-    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    if not np.isfinite(g).all():
+        bad = np.argwhere(~np.isfinite(g))
+        rows = sorted({tuple(int(i) for i in ix[:-1]) for ix in bad})
+        raise AssertionError(f"{what}: non-finite output at {len(bad)} elements, "
+                             f"rows (all indices but the last) {rows[:12]}{' ...' if len(rows) > 12 else ''}")
     err = np.abs(g - ref)
     stats = {"max_abs": float(err.max(initial=0.0)), "mean_abs": float(err.mean()) if err.size else 0.0}
     if dtype == torch.float32:

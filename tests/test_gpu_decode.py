@@ -336,3 +336,24 @@ def test_decode_unusual_scales(scale, dt):
     announce(f"decode scale={scale} {dt}")
     x = synth.decode_inputs(2, 32, 8, 128, 600, dtype=dt, seed=17, device=DEV, seqlens=[600, 345])
     assert_close(_run(x, scale), _oracle(x, scale), x["q"].dtype, f"scale={scale}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_split_merge_ignores_stale_workspace(dt):
+    """The merge reads the partial slots of splits that did not run in this call
+    (ragged lengths leave late splits empty); those slots hold whatever an
+    earlier call left there.  Filled with NaN bit patterns (the arrival counters
+    zeroed, as the library requires), the output must still be exact-to-tolerance
+    and finite."""
+    announce(f"decode stale workspace {dt}")
+    B, H, G, d, n_max = 3, 32, 8, 128, 777
+    x = synth.decode_inputs(B, H, G, d, n_max, dtype=dt, seed=23, device=DEV, seqlens=[777, 300, 5],
+                            nan_tail=True)
+    scale = synth.scale_for(d)
+    need = gqa.decode_workspace_bytes(B, H, G, d, n_max, 0)
+    assert need > 65536
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)     # float32 NaN everywhere
+    ws[:65536] = 0                                                     # counter header
+    out = gqa.decode(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(out, _oracle(x, scale), x["q"].dtype, "stale workspace")
