@@ -139,12 +139,15 @@ def decode_workspace_bytes(B: int, H: int, G: int, d: int, n_max: int, num_split
 
 
 def _cached_workspace(dev, need: int) -> torch.Tensor:
-    """A zero-filled workspace per device, grown on demand (the library keeps its
-    counter header zero between calls, so it is cleared only when allocated)."""
-    t = _workspaces.get(dev)
+    """A zero-filled workspace per (device, current stream), grown on demand (the
+    library keeps its counter header zero between calls, so it is cleared only
+    when allocated).  Calls that overlap on one workspace would race, so calls
+    on different streams get different workspaces."""
+    key = (str(dev), _stream_handle(dev))
+    t = _workspaces.get(key)
     if t is None or t.numel() < need:
         t = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=dev)
-        _workspaces[dev] = t
+        _workspaces[key] = t
     return t
 
 

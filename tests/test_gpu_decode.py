@@ -357,3 +357,26 @@ def test_split_merge_ignores_stale_workspace(dt):
     out = gqa.decode(x["q"], x["k_cache"], x["v_cache"], x["seqlens"], scale=scale, workspace=ws)
     torch.cuda.synchronize()
     assert_close(out, _oracle(x, scale), x["q"].dtype, "stale workspace")
+
+
+def test_decode_on_two_streams():
+    """Split decodes issued alternately on two streams (default priority) may run
+    at the same time; each stream gets its own cached workspace, so both results
+    are right."""
+    announce("decode two streams")
+    xa = synth.decode_inputs(4, 32, 8, 128, 900, dtype="bf16", seed=31, device=DEV, seqlens=[900, 513, 260, 7])
+    xb = synth.decode_inputs(4, 32, 8, 128, 900, dtype="bf16", seed=32, device=DEV, seqlens=[31, 899, 700, 450])
+    scale = synth.scale_for(128)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs_a, outs_b = [], []
+    torch.cuda.synchronize()
+    for _ in range(6):
+        with torch.cuda.stream(sa):
+            outs_a.append(gqa.decode(xa["q"], xa["k_cache"], xa["v_cache"], xa["seqlens"], scale=scale))
+        with torch.cuda.stream(sb):
+            outs_b.append(gqa.decode(xb["q"], xb["k_cache"], xb["v_cache"], xb["seqlens"], scale=scale))
+    torch.cuda.synchronize()
+    ra, rb = _oracle(xa, scale), _oracle(xb, scale)
+    for oa, ob in zip(outs_a, outs_b):
+        assert_close(oa, ra, torch.bfloat16, "stream a")
+        assert_close(ob, rb, torch.bfloat16, "stream b")
