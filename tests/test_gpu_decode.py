@@ -380,3 +380,18 @@ def test_decode_on_two_streams():
     for oa, ob in zip(outs_a, outs_b):
         assert_close(oa, ra, torch.bfloat16, "stream a")
         assert_close(ob, rb, torch.bfloat16, "stream b")
+
+
+def test_split_decode_beyond_counter_capacity():
+    """More (sequence, K/V head) units than the workspace has arrival counters
+    (16384): the split partials are then merged by the separate combine pass.
+    Checked on sampled sequences."""
+    announce("decode split, units beyond counter capacity")
+    B, H, G, d, n_max = 2100, 32, 8, 64, 64
+    rng = np.random.default_rng(5)
+    lens = [int(v) for v in rng.integers(0, n_max + 1, B)]
+    x = synth.decode_inputs(B, H, G, d, n_max, dtype="bf16", seed=41, device=DEV, seqlens=lens)
+    scale = synth.scale_for(d)
+    out = _run(x, scale, num_splits=2)
+    rows = [0, 1, 2, 777, 1500, 2099] + [int(i) for i in rng.integers(0, B, 10)]
+    assert_close(out[rows], _oracle(x, scale, rows=rows), torch.bfloat16, "combine pass")
