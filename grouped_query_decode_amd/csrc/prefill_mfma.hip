@@ -18,12 +18,13 @@
 //   mask j > i on tiles that reach the diagonal; online softmax in base 2,
 //   float32, one query row per lane column (max/sum in-lane plus one exchange)
 //   O^T[dim][row] += V^T[dim][key] P^T[key][row] 32x32x16 MFMA (4 x 4),
-//                   A = V^T from LDS (transposed once per workgroup when the
-//                   tile is staged), B = the 16-bit weights, already in place
+//                   A = V^T read from the row-major V tile in LDS by
+//                   transposing reads, B = the 16-bit weights, already in place
 //
-// K/V tiles are double-buffered in LDS (layouts below): the next tiles'
-// global loads are issued before the current tile's math and land in the freed
-// buffers afterwards, one barrier per tile; the weighted sum of a tile is
+// K/V tiles are double-buffered in LDS (layouts below) and arrive by buffer
+// loads that write LDS directly, with no register staging: the next tiles'
+// loads are issued at the start of an iteration into the buffers the previous
+// one freed and land during its math, one barrier per tile; the weighted sum of a tile is
 // deferred by one iteration so that each iteration hands the matrix unit and
 // the vector unit independent work.  Softmax work per score: one FMA
 // (scale folded in), one hardware exp2 (weights below 2^-126 may flush to
@@ -39,6 +40,8 @@
 #include "device_common.h"
 #include "internal.h"
 
+#include <type_traits>
+
 namespace gqa {
 namespace {
 
@@ -50,26 +53,37 @@ constexpr int kXcds = 8;
 constexpr float kLazyLog2 = 8.f;
 
 
-// LDS tiles (64 banks of 4 bytes):
-//  * K row-major, rows padded by 16 bytes: 16 consecutive rows read at one
-//    column with 16-byte reads cover all banks.
-//  * V stored transposed, V^T[dim][key], rows of 64 keys padded by 16 bytes,
-//    keys permuted inside a row (vt_pos) so that the 8 keys one lane feeds to
-//    one PV k-step are contiguous: the PV operand is one 16-byte read, 16
-//    consecutive dims of a read cover all banks, and the transposing 4-byte
-//    writes of a wave (two dim rows, 64 keys) cover all banks too.
-// Every operand address is a per-lane base plus a compile-time offset.
+// LDS tiles, 64 banks of 4 bytes, rows unpadded and 16-byte chunks XOR-permuted
+// inside each row so that the operand reads below hit all banks:
+//  * K row-major: chunk c of key r sits at c ^ ksw(r).
+//  * V row-major: chunk c of key k sits at c ^ vsw(k); the PV operand (V^T)
+//    comes from transposing LDS reads.
+// Tiles arrive by buffer loads that write LDS directly (16 bytes per lane, lane
+// i at base + 16 i): each lane fetches the global chunk that belongs at its
+// LDS position, so the permutation costs nothing at write time.
 template <int D>
 struct PCfg {
   static constexpr int kSteps = D / 16;          // QK k-steps (k = 16)
   static constexpr int kColBlocks = D / 32;      // PV output blocks of 32 dims
   static constexpr int kChunks = D / 8;          // 16-byte chunks per row
-  static constexpr int kKPitch = D * 2 + 16;
-  static constexpr int kVtPitch = kKT * 2 + 16;
-  static constexpr int kKBytes = kKT * kKPitch;
-  static constexpr int kVBytes = D * kVtPitch;
-  static constexpr int kBufBytes = kKBytes + kVBytes;
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = kKT * kRowBytes;
+  static constexpr int kDma = kTileBytes / 1024; // 64-lane x 16-byte loads per tile
 };
+template <int D>
+__device__ __forceinline__ int ksw(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int vsw(int k) { return D == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): within each 16-lane
+// group, lanes 4e..4e+3 each address 4 consecutive 16-bit values of row e of
+// a 4 x 16 block, and lane i receives column i of the 4 rows.
+__device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(const_cast<char*>(p)));
+}
 
 // 32x32x16 MFMA on raw 16-bit operands: bfloat16 or IEEE half (DT).
 template <int DT>
@@ -82,24 +96,24 @@ __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-// Position of key kl (0..63) inside a V^T row: kl = 16u + 8a + 4h + b is
-// stored at 16u + 8h + 4a + b, so that the keys one lane (k-slot half h) feeds
-// to PV k-step u -- 16u + 8*(e/4) + 4h + e%4, e = 0..7 -- are contiguous.
-__device__ __forceinline__ int vt_pos(int kl) {
-  return (kl & ~15) | ((kl & 4) << 1) | ((kl & 8) >> 1) | (kl & 3);
-}
+template <int V> using IC = std::integral_constant<int, V>;
 
 template <int D, int NW, int DT>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillProblem p) {
   using C = PCfg<D>;
   using H16 = Half16<DT>;
-  constexpr int kThreads = 64 * NW;
-  constexpr int kLoads = kKT * C::kChunks / kThreads;     // per thread per tile (K and V each)
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kBufBytes];   // K0 K1 V0 V1
+  static_assert(C::kDma % NW == 0, "tile loads split evenly over the waves");
+  constexpr int kDmaW = C::kDma / NW;            // per wave per tile (K and V each)
+  // separate arrays per slot: the compiler then knows which loads in flight
+  // each LDS read may depend on
+  __shared__ __attribute__((aligned(16))) char sk0[C::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char sk1[C::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char sv0[C::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char sv1[C::kTileBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int h2 = lane >> 5;
 
@@ -138,6 +152,44 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   const int kv_end = min(ctx + t_last, last_pos) + 1;       // positions any row here sees
   const int n_kt = (kv_end + kKT - 1) / kKT;
 
+  const int64_t kv_row = p.kv_pstride;               // elements between positions
+  const uint16_t* kbase = p.k + int64_t(b) * p.kv_bstride + int64_t(g) * p.kv_gstride;
+  const uint16_t* vbase = p.v + int64_t(b) * p.kv_bstride + int64_t(g) * p.kv_gstride;
+  // Positions [0, kv_end) of this (b, g) through buffer resources that end
+  // there: loads past the end write zeros to LDS without a memory access, so
+  // the tile loads need no per-lane branches.  (The host keeps every offset
+  // below 2^31.)
+  const int row_bytes = int(kv_row) * 2;
+  const uint32_t kv_bytes = uint32_t((kv_end - 1) * row_bytes + D * 2);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kbase), 0, kv_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vbase), 0, kv_bytes, 0x00020000);
+  // this lane's source offsets within a tile: LDS chunk position s of row r
+  // holds global chunk s ^ swizzle(r)
+  int koff[kDmaW], voff[kDmaW];
+#pragma unroll
+  for (int i = 0; i < kDmaW; ++i) {
+    const int pos = (wave * kDmaW + i) * 64 + lane;
+    const int r = pos / C::kChunks, s = pos % C::kChunks;
+    koff[i] = r * row_bytes + ((s ^ ksw<D>(r)) << 4);
+    voff[i] = r * row_bytes + ((s ^ vsw<D>(r)) << 4);
+  }
+  auto tile_load = [&](__amdgpu_buffer_rsrc_t rs, const int* off, int kt, char* dst) {
+    const int base = kt * kKT * row_bytes;
+#pragma unroll
+    for (int i = 0; i < kDmaW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(dst + (wave * kDmaW + i) * 1024), 16,
+          base + off[i], 0, 0, 0);
+  };
+  auto kslot = [&](auto P) -> char* {
+    if constexpr (decltype(P)::value == 0) return sk0; else return sk1;
+  };
+  auto vslot = [&](auto P) -> char* {
+    if constexpr (decltype(P)::value == 0) return sv0; else return sv1;
+  };
+
   // queries: B operand, lane column = row l32, k-slot group h2 -> dims 16*ks + 8*h2 .. +7.
   // A negative scale is folded into the queries (exact sign flip).
   const uint32_t qsign = p.scale < 0.f ? 0x80008000u : 0u;
@@ -146,12 +198,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   const float c2 = p.scale == 0.f ? 1e-30f : fabsf(p.scale) * kLog2e;
   u32x4_t qop[C::kSteps];
   {
-    const bool rv = t_row < p.T;
-    const uint16_t* qrow = p.q + ((int64_t(b) * p.T + (rv ? t_row : 0)) * p.hm.q_heads + p.hm.q_head(g, qr)) * D;
+    const bool rvq = t_row < p.T;
+    const uint16_t* qrow = p.q + ((int64_t(b) * p.T + (rvq ? t_row : 0)) * p.hm.q_heads + p.hm.q_head(g, qr)) * D;
 #pragma unroll
     for (int ks = 0; ks < C::kSteps; ++ks) {
       u32x4_t w = {0u, 0u, 0u, 0u};
-      if (rv) w = ld16(qrow + 16 * ks + 8 * h2);
+      if (rvq) w = ld16(qrow + 16 * ks + 8 * h2);
       w ^= u32x4_t{qsign, qsign, qsign, qsign};
       qop[ks] = w;
     }
@@ -165,90 +217,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   float mrun = -INFINITY;     // running max of the raw scores of this lane's row
   float lrun = 0.f;           // this lane's share of the normaliser
 
-  const int64_t kv_row = p.kv_pstride;               // elements between positions
-  const uint16_t* kbase = p.k + int64_t(b) * p.kv_bstride + int64_t(g) * p.kv_gstride;
-  const uint16_t* vbase = p.v + int64_t(b) * p.kv_bstride + int64_t(g) * p.kv_gstride;
-
-  u32x4_t kreg[kLoads];
-  // thread's first (position, chunk) of a tile; the others are kRowStep positions apart
-  const int kl0 = tid / C::kChunks;
-  const int ch0 = tid % C::kChunks;
-  constexpr int kRowStep = kThreads / C::kChunks;
-  // Positions [0, kv_end) of this (b, g) through buffer resources that end
-  // there: loads past the end return zeros without a memory access, so the
-  // tile loads need no per-lane branches.  (The host keeps every offset below
-  // 2^31.)
-  const int row_bytes = int(kv_row) * 2;
-  const uint32_t kv_bytes = uint32_t((kv_end - 1) * row_bytes + D * 2);
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kbase), 0, kv_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vbase), 0, kv_bytes, 0x00020000);
-  auto load_rows = [&](int kt, u32x4_t* reg) {
-    const int off0 = (kt * kKT + kl0) * row_bytes + ch0 * 16;
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-      reg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off0 + i * kRowStep * row_bytes, 0, 0);
-  };
-  // V tiles: each thread loads key pairs (2p, 2p+1) x one 16-byte chunk; a
-  // wave's lanes cover 32 pairs x 2 chunks (so that its transposed writes
-  // below hit all banks)
-  constexpr int kVPairItems = 32 * C::kChunks;
-  constexpr int kVItems = (kVPairItems + kThreads - 1) / kThreads;
-  u32x4_t vpr[kVItems][2];
-  auto load_vpairs = [&](int kt) {
-#pragma unroll
-    for (int j = 0; j < kVItems; ++j) {
-      const int item = tid + j * kThreads;
-      const int pr = item & 31;
-      const int ch = 2 * (item >> 6) + ((item >> 5) & 1);
-      const int off = (kt * kKT + 2 * pr) * row_bytes + ch * 16;
-      u32x4_t w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
-      if (kVItems * kThreads == kVPairItems || item < kVPairItems) {   // uniform per wave
-        w0 = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
-        w1 = __builtin_amdgcn_raw_buffer_load_b128(rv, off + row_bytes, 0, 0);
-      }
-      vpr[j][0] = w0;
-      vpr[j][1] = w1;
-    }
-  };
-  auto store_vt = [&](char* dst) {
-#pragma unroll
-    for (int j = 0; j < kVItems; ++j) {
-      const int item = tid + j * kThreads;
-      if (kVItems * kThreads == kVPairItems || item < kVPairItems) {
-        const int pr = item & 31;
-        const int ch = 2 * (item >> 6) + ((item >> 5) & 1);
-        char* col = dst + (8 * ch) * C::kVtPitch + vt_pos(2 * pr) * 2;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // (V[2p][8ch + 2e], V[2p+1][8ch + 2e]) and the odd dims
-          *reinterpret_cast<uint32_t*>(col + (2 * e) * C::kVtPitch) =
-              __builtin_amdgcn_perm(vpr[j][1][e], vpr[j][0][e], 0x05040100u);
-          *reinterpret_cast<uint32_t*>(col + (2 * e + 1) * C::kVtPitch) =
-              __builtin_amdgcn_perm(vpr[j][1][e], vpr[j][0][e], 0x07060302u);
-        }
-      }
-    }
-  };
-  // LDS: K slots 0, 1 then V^T slots 0, 1 (see PCfg)
-  auto kslot = [&](int s) { return smem + s * C::kKBytes; };
-  auto vslot = [&](int s) { return smem + 2 * C::kKBytes + s * C::kVBytes; };
-  auto store_rows = [&](char* dst, int pitch, const u32x4_t* reg) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-      *reinterpret_cast<u32x4_t*>(dst + (kl0 + i * kRowStep) * pitch + ch0 * 16) = reg[i];
-  };
-
   // scores of one tile: lane holds S^T[key0 + 32*kb + 8*(r/4) + 4*h2 + r%4][t_row];
-  // two independent accumulator chains (key blocks kb = 0, 1) interleaved
+  // two independent accumulator chains (key blocks kb = 0, 1) interleaved.
+  // K operand: row l32 (+32), chunk 2 ks + h2, permuted: byte offset
+  // (32 ks + 16 h2) ^ 16 ksw(l32) = kx ^ 32 ks inside the row.
+  const int kx = l32 * C::kRowBytes + ((h2 ^ ksw<D>(l32)) << 4);
   auto qk = [&](const char* sk, f32x16_t* sc) {
-    const char* krow0 = sk + l32 * C::kKPitch + h2 * 16;
     const f32x16_t zero = {};
 #pragma unroll
     for (int ks = 0; ks < C::kSteps; ++ks) {
-      const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(krow0 + ks * 32);
-      const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(krow0 + 32 * C::kKPitch + ks * 32);
+      const char* a = sk + (kx ^ (32 * ks));
+      const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(a);
+      const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(a + 32 * C::kRowBytes);
       sc[0] = mfma32<DT>(k0, qop[ks], ks == 0 ? zero : sc[0]);
       sc[1] = mfma32<DT>(k1, qop[ks], ks == 0 ? zero : sc[1]);
     }
@@ -301,17 +281,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
     mrun = mref;
   };
 
-  // O^T += V^T P^T: A = V^T[32*cb + l32][keys of k-step u, half h2], one
-  // 16-byte read (keys stored contiguously, see vt_pos)
-  const int vt_lane = l32 * C::kVtPitch + h2 * 16;
+  // O^T += V^T P^T.  A operand for k-step u, lane (l32, h2): V[key][32 cb +
+  // l32] for keys 16u + 8*(e/4) + 4*h2 + e%4, e = 0..7 -- two transposing
+  // reads of 4 keys each.  In the read, lane l32 % 16 = 4 e4 + j4 addresses key
+  // 4 h2 + e4 (+16u, +8) at dims 32 cb + 16 (l32 / 16) + 4 j4, a permuted byte
+  // offset of vx ^ 64 cb.
+  const int e4 = (l32 >> 2) & 3, j4 = l32 & 3;
+  const int vx = (4 * h2 + e4) * C::kRowBytes +
+                 (64 * (D == 128 ? e4 : (e4 >> 1)) + 32 * (l32 >> 4) + 8 * j4);
   auto pv = [&](const u32x4_t* pop, const char* sv) {
-    const char* vlane = sv + vt_lane;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       u32x4_t vop[C::kColBlocks];
 #pragma unroll
-      for (int cb = 0; cb < C::kColBlocks; ++cb)
-        vop[cb] = *reinterpret_cast<const u32x4_t*>(vlane + (32 * cb) * C::kVtPitch + 32 * u);
+      for (int cb = 0; cb < C::kColBlocks; ++cb) {
+        const char* a = sv + (vx ^ (64 * cb)) + 16 * u * C::kRowBytes;
+        const i16x4_t lo = lds_read_tr16(a);
+        const i16x4_t hi = lds_read_tr16(a + 8 * C::kRowBytes);
+        vop[cb] = __builtin_bit_cast(u32x4_t, i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      }
 #pragma unroll
       for (int cb = 0; cb < C::kColBlocks; ++cb) acc[cb] = mfma32<DT>(vop[cb], pop[u], acc[cb]);
     }
@@ -321,6 +309,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
 #pragma unroll
     for (int cb = 0; cb < C::kColBlocks; ++cb) acc[cb] *= alpha;
   };
+  // every wave's tile loads have landed, then all waves meet
+  auto tile_barrier = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
 
   // Software pipeline over key tiles.  Iteration t issues, as one scheduling
   // region with no branch inside: the score MFMAs of tile t+1, the weighted
@@ -329,25 +322,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   // of the same wave.  When tile t moved a row's reference maximum (rare),
   // the running output -- which by then holds the tiles up to t-1 -- is
   // rescaled at the end of the iteration, before tile t's weights are added
-  // at the next one.  LDS: K slot (t+1)&1 holds K(t+1), V slot (t+1)&1 holds V(t-1);
-  // the global loads of K(t+2) and V(t) land in the slots t&1 this iteration
-  // freed.  Tiles before t_split lie wholly below every row of the workgroup
-  // (no mask) and have a successor; the rest take the masked path.
+  // at the next one.  LDS: K slot (t+1)&1 holds K(t+1), V slot (t+1)&1 holds
+  // V(t-1); the loads of K(t+2) and V(t) go, at the start of the iteration,
+  // to the slots t&1 the previous iteration freed, and land during it.  Tiles
+  // before t_split lie wholly below every row of the workgroup (no mask) and
+  // have a successor; the rest take the masked path.  The slot parity P = t&1
+  // is a compile-time constant at every call site.
   const int t_split = min(n_kt - 1, min(ctx + qt * rows_wg, last_pos) / kKT);
-  {
-    // both first K tiles in flight at once (tile 1 reads as zeros past the end)
-    u32x4_t kreg1[kLoads];
-    load_rows(0, kreg);
-    load_rows(1, kreg1);
-    store_rows(kslot(0), C::kKPitch, kreg);
-    store_rows(kslot(1), C::kKPitch, kreg1);
-  }
-  __syncthreads();
+  tile_load(rk, koff, 0, sk0);
+  tile_load(rk, koff, 1, sk1);     // (reads as zeros past the end)
+  tile_barrier();
   // Two score buffers alternate between "this tile" and "next tile" (the
   // loops below are unrolled by two), so no copy sits between a tile's score
   // MFMAs and its softmax.
   f32x16_t sa[2], sb[2];
-  qk(kslot(0), sa);
+  qk(sk0, sa);
   // every wave has read K(0) before the first iteration overwrites its slot
   __syncthreads();
   u32x4_t pprev[4];
@@ -356,61 +345,59 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
 
   // one unmasked iteration (with_pv is a constant at each call site, so the
   // region below has no branch); cur holds tile t's scores, nxt receives t+1's
-  auto iter_unmasked = [&](int t, bool with_pv, f32x16_t* cur, f32x16_t* nxt) {
-    load_rows(min(t + 2, n_kt - 1), kreg);
-    load_vpairs(t);
-    qk(kslot((t + 1) & 1), nxt);
-    if (with_pv) pv(pprev, vslot((t + 1) & 1));
+  auto iter_unmasked = [&](int t, auto P, bool with_pv, f32x16_t* cur, f32x16_t* nxt) {
+    constexpr int Q = 1 - decltype(P)::value;
+    tile_load(rk, koff, min(t + 2, n_kt - 1), kslot(P));
+    tile_load(rv, voff, t, vslot(P));
+    qk(kslot(IC<Q>{}), nxt);
+    if (with_pv) pv(pprev, vslot(IC<Q>{}));
     softmax(cur, t * kKT, false, pprev, alpha_prev, rescale_prev);
-    store_rows(kslot(t & 1), C::kKPitch, kreg);    // K(t) was read by the scores of tile t
-    store_vt(vslot(t & 1));                        // V(t-2) was summed at iteration t-1
     // the weights are made here, ahead of the branch (not sunk into the next
     // iteration, which would leave the matrix work above without vector work)
 #pragma unroll
     for (int u = 0; u < 4; ++u) asm volatile("" ::"v"(pprev[u]));
     if (rescale_prev) rescale_acc(alpha_prev);
-    __syncthreads();
+    tile_barrier();
   };
   // one iteration on a tile that may reach the diagonal
-  auto iter_masked = [&](int t, f32x16_t* cur, f32x16_t* nxt) {
-    if (t + 2 < n_kt) load_rows(t + 2, kreg);
-    load_vpairs(t);
+  auto iter_masked = [&](int t, auto P, f32x16_t* cur, f32x16_t* nxt) {
+    constexpr int Q = 1 - decltype(P)::value;
+    if (t + 2 < n_kt) tile_load(rk, koff, t + 2, kslot(P));
+    tile_load(rv, voff, t, vslot(P));
     const bool next_active = t + 1 < n_kt && (t + 1) * kKT <= a_wave;
-    if (next_active) qk(kslot((t + 1) & 1), nxt);
-    if (t > 0 && (t - 1) * kKT <= a_wave) pv(pprev, vslot((t + 1) & 1));
+    if (next_active) qk(kslot(IC<Q>{}), nxt);
+    if (t > 0 && (t - 1) * kKT <= a_wave) pv(pprev, vslot(IC<Q>{}));
     if (t * kKT <= a_wave) {
       softmax(cur, t * kKT, true, pprev, alpha_prev, rescale_prev);
     } else {
       rescale_prev = false;
     }
-    if (t + 2 < n_kt) store_rows(kslot(t & 1), C::kKPitch, kreg);
-    store_vt(vslot(t & 1));
     if (rescale_prev) rescale_acc(alpha_prev);
-    __syncthreads();
+    tile_barrier();
   };
   // tile t's scores are in sa for even t, in sb for odd t
   int t = 0;
   if (t_split > 0) {
-    iter_unmasked(0, false, sa, sb);
+    iter_unmasked(0, IC<0>{}, false, sa, sb);
     for (t = 1; t + 1 < t_split; t += 2) {
-      iter_unmasked(t, true, sb, sa);
-      iter_unmasked(t + 1, true, sa, sb);
+      iter_unmasked(t, IC<1>{}, true, sb, sa);
+      iter_unmasked(t + 1, IC<0>{}, true, sa, sb);
     }
     if (t < t_split) {
-      iter_unmasked(t, true, sb, sa);
+      iter_unmasked(t, IC<1>{}, true, sb, sa);
       ++t;
     }
   }
   if (t < n_kt && (t & 1)) {
-    iter_masked(t, sb, sa);
+    iter_masked(t, IC<1>{}, sb, sa);
     ++t;
   }
   for (; t < n_kt; t += 2) {                       // tiles that reach the diagonal
-    iter_masked(t, sa, sb);
-    if (t + 1 < n_kt) iter_masked(t + 1, sb, sa);
+    iter_masked(t, IC<0>{}, sa, sb);
+    if (t + 1 < n_kt) iter_masked(t + 1, IC<1>{}, sb, sa);
   }
   // the last tile's weighted sum (any rescale it needs was applied above)
-  if ((n_kt - 1) * kKT <= a_wave) pv(pprev, vslot((n_kt - 1) & 1));
+  if ((n_kt - 1) * kKT <= a_wave) pv(pprev, ((n_kt - 1) & 1) ? sv1 : sv0);
 
   const float l = lrun + shfl_xor(lrun, 32);
   if (t_row < p.T) {
