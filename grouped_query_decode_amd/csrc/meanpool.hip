@@ -7,9 +7,10 @@
 // HBM-bound: every input element is read once and every output element
 // written once.  Each thread owns 8 consecutive elements of one group's output
 // (16-byte bfloat16 or 2 x 16-byte float32 accesses), reads the same 8 elements
-// of the group's n_rep heads, sums in float32, divides once (correctly
-// rounded) and rounds once to the storage type.  A grid-stride loop covers the
-// output; a scalar kernel handles sizes that are not a multiple of 8.
+// of the group's n_rep heads (up to 8 loads in flight, non-temporal: each input
+// element is read once), sums in float32 in head order, divides once
+// (correctly rounded) and rounds once to the storage type.  A grid-stride loop
+// covers the output; a scalar kernel handles sizes that are not a multiple of 8.
 
 #include "device_common.h"
 #include "internal.h"
@@ -17,48 +18,70 @@
 namespace gqa {
 namespace {
 
+// Adds heads k0 .. k0+NB-1 of group g (8 elements at e8) to acc: all NB loads
+// are issued before the first add, so NB requests per thread are in flight;
+// the adds run in head order (the same rounding as one head at a time).
+template <int DT, int NB>
+__device__ __forceinline__ void add_heads(const MeanpoolProblem& p, int64_t g, int64_t e8, int k0, float* acc) {
+  if constexpr (DT != kF32) {
+    u32x4_t w[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      w[j] = ld16_stream(static_cast<const uint16_t*>(p.w_in) + (g * p.n_rep + k0 + j) * p.per_head_elems + e8 * 8);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc[2 * t] += Half16<DT>::lo(w[j][t]);
+        acc[2 * t + 1] += Half16<DT>::hi(w[j][t]);
+      }
+  } else {
+    u32x4_t a[NB], b[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const float* src = static_cast<const float*>(p.w_in) + (g * p.n_rep + k0 + j) * p.per_head_elems + e8 * 8;
+      a[j] = ld16_stream(src);
+      b[j] = ld16_stream(src + 4);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc[t] += __uint_as_float(a[j][t]);
+        acc[4 + t] += __uint_as_float(b[j][t]);
+      }
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void meanpool_vec8_kernel(MeanpoolProblem p) {
   const int64_t vec_per_head = p.per_head_elems / 8;
   const int64_t total = int64_t(p.G) * vec_per_head;
-  const float inv_div = float(p.n_rep);
+  const float n = float(p.n_rep);
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
        i += int64_t(gridDim.x) * blockDim.x) {
     const int64_t g = i / vec_per_head;
     const int64_t e8 = i - g * vec_per_head;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < p.n_rep; ++k) {
-      const int64_t elem = (g * p.n_rep + k) * p.per_head_elems + e8 * 8;
-      if constexpr (DT != kF32) {
-        const u32x4_t w = ld16(static_cast<const uint16_t*>(p.w_in) + elem);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          acc[2 * t] += Half16<DT>::lo(w[t]);
-          acc[2 * t + 1] += Half16<DT>::hi(w[t]);
-        }
-      } else {
-        const float* src = static_cast<const float*>(p.w_in) + elem;
-        const u32x4_t a = ld16(src);
-        const u32x4_t b = ld16(src + 4);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          acc[t] += __uint_as_float(a[t]);
-          acc[4 + t] += __uint_as_float(b[t]);
-        }
-      }
+    int k = 0;
+    for (; k + 8 <= p.n_rep; k += 8) add_heads<DT, 8>(p, g, e8, k, acc);
+    if (k + 4 <= p.n_rep) {
+      add_heads<DT, 4>(p, g, e8, k, acc);
+      k += 4;
     }
+    for (; k < p.n_rep; ++k) add_heads<DT, 1>(p, g, e8, k, acc);
     const int64_t oel = g * p.per_head_elems + e8 * 8;
     if constexpr (DT != kF32) {
       u32x4_t w;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) w[t] = Half16<DT>::pack2(acc[2 * t] / inv_div, acc[2 * t + 1] / inv_div);
+      for (int t = 0; t < 4; ++t) w[t] = Half16<DT>::pack2(acc[2 * t] / n, acc[2 * t + 1] / n);
       st16(static_cast<uint16_t*>(p.w_out) + oel, w);
     } else {
       u32x4_t a, b;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        a[t] = __float_as_uint(acc[t] / inv_div);
-        b[t] = __float_as_uint(acc[4 + t] / inv_div);
+        a[t] = __float_as_uint(acc[t] / n);
+        b[t] = __float_as_uint(acc[4 + t] / n);
       }
       float* dst = static_cast<float*>(p.w_out) + oel;
       st16(dst, a);
