@@ -44,6 +44,7 @@ CHUNK_CASES = [
     (3, 50, 8, 2, 128, 120, [100, -4, 70], "bf16"),      # past the cache (clamped), negative ctx
     (2, 1, 32, 8, 128, 500, [0, 499], "bf16"),           # one row: a decode step
     (2, 90, 8, 2, 128, 300, [10, 200], "f16"),
+    (2, 70, 16, 4, 64, 400, [33, 250], "f16"),         # d = 64, n_rep = 4
     (2, 45, 8, 2, 64, 200, [20, 150], "f32"),
 ]
 

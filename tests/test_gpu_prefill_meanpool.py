@@ -31,6 +31,8 @@ PREFILL_CASES = [
     (1, 333, 32, 8, 128, "bf16"),
     (2, 130, 8, 8, 64, "bf16"),      # n_rep = 1
     (2, 97, 8, 4, 64, "bf16"),       # n_rep = 2
+    (2, 150, 16, 4, 64, "bf16"),     # n_rep = 4 at d = 64 (4 heads per workgroup)
+    (1, 200, 32, 4, 64, "bf16"),     # n_rep = 8 at d = 64
     (1, 150, 32, 1, 128, "bf16"),    # n_rep = 32
     (1, 64, 24, 8, 128, "bf16"),     # n_rep = 3 (vector units)
     (1, 1, 8, 2, 128, "bf16"),       # single position
