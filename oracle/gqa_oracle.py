@@ -23,7 +23,7 @@ Sources (cited by title and section):
 * The CSDN interview explainer on GQA, section 03 (repeating each K/V head
   n_rep times so that an MHA kernel can be reused).
 
-Readings taken where the pages are silent (each is also listed in the design doc):
+Readings taken where the pages are silent:
 
 * Group membership is contiguous: query head h belongs to K/V head
   floor(h * G / H).  The tutorial's example puts heads 1-4 in group 1 and
