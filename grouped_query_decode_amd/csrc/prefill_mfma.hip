@@ -9,9 +9,10 @@
 // Work unit: one workgroup of NW waves (8 at d = 128, 4 at d = 64) per (b, g,
 // head quad, query tile).  Each wave owns 32 query positions of one head; the
 // waves of a workgroup cover 4 heads of one group x NW/4 consecutive
-// 32-position blocks (n_rep >= 4), or 2 heads x NW/2 blocks (n_rep = 2), or 1
-// head x NW blocks (n_rep = 1), so every K/V tile staged in LDS is used by
-// 32*NW query rows.  Per 64-key tile and wave:
+// 32-position blocks (n_rep >= 3; when n_rep is not a multiple of 4 the
+// group's last quad is padded with waves that store nothing), or 2 heads x
+// NW/2 blocks (n_rep = 2), or 1 head x NW blocks (n_rep = 1), so every K/V
+// tile staged in LDS is used by 32*NW query rows.  Per 64-key tile and wave:
 //
 //   S^T[key][row] = K[key][:] . Q[row][:]        32x32x16 16-bit MFMA (2 x 8),
 //                   A = K tile from LDS, B = the wave's queries (registers)
@@ -119,9 +120,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   const int l32 = lane & 31;
   const int h2 = lane >> 5;
 
-  const int nre = p.n_rep < 4 ? p.n_rep : 4;      // heads per workgroup
+  const int nre = p.n_rep <= 2 ? p.n_rep : 4;     // head slots per workgroup
   const int tb_per_wg = NW / nre;                  // 32-position blocks per workgroup
-  const int n_hq = p.n_rep / nre;
+  const int n_hq = (p.n_rep + nre - 1) / nre;      // (the last quad may be padded)
   const int rows_wg = kQT * tb_per_wg;
   const int n_qt = (p.T + rows_wg - 1) / rows_wg;
   const int units = p.B * p.G * n_hq;
@@ -143,6 +144,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   const int b = unit / (n_hq * p.G);
 
   const int qr = hq * nre + (wave % nre);          // query of the group this wave owns
+  // A padding slot of the last quad (qr >= n_rep) computes on a copy of the
+  // group's last query and stores nothing: the workgroup's tile loads and
+  // barriers stay the same for every wave.
+  const bool q_valid = qr < p.n_rep;
   const int t_base = qt * rows_wg + (wave / nre) * kQT;
   const int t_row = t_base + l32;                  // this lane's query row
   const int t_last = min(p.T, (qt + 1) * rows_wg) - 1;
@@ -201,7 +206,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   u32x4_t qop[C::kSteps];
   {
     const bool rvq = t_row < p.T;
-    const uint16_t* qrow = p.q + ((int64_t(b) * p.T + (rvq ? t_row : 0)) * p.hm.q_heads + p.hm.q_head(g, qr)) * D;
+    const uint16_t* qrow = p.q + ((int64_t(b) * p.T + (rvq ? t_row : 0)) * p.hm.q_heads + p.hm.q_head(g, q_valid ? qr : p.n_rep - 1)) * D;
 #pragma unroll
     for (int ks = 0; ks < C::kSteps; ++ks) {
       u32x4_t w = {0u, 0u, 0u, 0u};
@@ -418,7 +423,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   if ((n_kt - 1) * kKT <= a_wave) pv(pprev, ((n_kt - 1) & 1) ? sv1 : sv0);
 
   const float l = lrun + shfl_xor(lrun, 32);
-  if (t_row < p.T) {
+  if (t_row < p.T && q_valid) {
     const float inv = 1.f / l;
     uint16_t* orow = p.out + ((int64_t(b) * p.T + t_row) * p.hm.o_heads + p.hm.o_head(g, qr)) * D;
 #pragma unroll
@@ -438,16 +443,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
 bool prefill_mfma_supports(int n_rep, int d, int kv_cap, int64_t kv_pstride) {
   // byte offsets of the K/V buffer loads (up to a tile past the end) stay below 2^31
   const int64_t reach = (int64_t(kv_cap) + 2 * kKT) * kv_pstride * 2;
-  return (d == 64 || d == 128) && (n_rep == 1 || n_rep == 2 || n_rep % 4 == 0) &&
+  return (d == 64 || d == 128) && n_rep >= 1 &&
          reach < (int64_t(1) << 31);
 }
 
 template <int D, int NW>
 hipError_t launch_d(const PrefillProblem& p, hipStream_t stream) {
-  const int nre = p.n_rep < 4 ? p.n_rep : 4;
+  const int nre = p.n_rep <= 2 ? p.n_rep : 4;
   const int rows_wg = kQT * (NW / nre);
   const int64_t n_qt = (p.T + rows_wg - 1) / rows_wg;
-  const int64_t blocks = n_qt * p.B * p.G * (p.n_rep / nre);
+  const int64_t blocks = n_qt * p.B * p.G * ((p.n_rep + nre - 1) / nre);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid = dim3(unsigned(blocks)), block = dim3(64 * NW);

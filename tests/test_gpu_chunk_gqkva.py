@@ -40,7 +40,8 @@ CHUNK_CASES = [
     (2, 64, 8, 8, 64, 300, [100, 236], "bf16"),          # n_rep = 1
     (2, 70, 8, 4, 64, 400, [5, 300], "bf16"),            # n_rep = 2
     (1, 40, 32, 1, 128, 200, [150], "bf16"),             # n_rep = 32
-    (2, 33, 24, 8, 128, 300, [7, 200], "bf16"),          # n_rep = 3: vector units
+    (2, 33, 24, 8, 128, 300, [7, 200], "bf16"),          # n_rep = 3: one padded head quad
+    (2, 60, 12, 2, 128, 300, [40, 200], "bf16"),         # n_rep = 6: second quad half padded
     (3, 50, 8, 2, 128, 120, [100, -4, 70], "bf16"),      # past the cache (clamped), negative ctx
     (2, 1, 32, 8, 128, 500, [0, 499], "bf16"),           # one row: a decode step
     (2, 90, 8, 2, 128, 300, [10, 200], "f16"),
@@ -153,7 +154,8 @@ GQKVA_PREFILL = [
     (2, 150, 2, 3, 128, "bf16"),
     (1, 200, 4, 2, 64, "bf16"),
     (2, 97, 1, 6, 128, "bf16"),
-    (1, 130, 3, 2, 128, "bf16"),        # 3 queries per K/V head: vector units
+    (1, 130, 3, 2, 128, "bf16"),        # 3 queries per K/V head: one padded quad
+    (1, 90, 5, 2, 64, "bf16"),          # 5 queries per K/V head: second quad padded
     (2, 100, 2, 3, 128, "f16"),
     (1, 70, 2, 3, 64, "f32"),
 ]

@@ -99,7 +99,7 @@ PREFILL_CASES = [
     (2, 130, 8, 8, 64),
     (2, 97, 8, 4, 64),
     (1, 150, 32, 1, 128),
-    (1, 64, 24, 8, 128),       # n_rep = 3: vector units
+    (1, 64, 24, 8, 128),       # n_rep = 3: one padded head quad
 ]
 
 

@@ -34,7 +34,10 @@ PREFILL_CASES = [
     (2, 150, 16, 4, 64, "bf16"),     # n_rep = 4 at d = 64 (4 heads per workgroup)
     (1, 200, 32, 4, 64, "bf16"),     # n_rep = 8 at d = 64
     (1, 150, 32, 1, 128, "bf16"),    # n_rep = 32
-    (1, 64, 24, 8, 128, "bf16"),     # n_rep = 3 (vector units)
+    (1, 64, 24, 8, 128, "bf16"),     # n_rep = 3: one padded head quad
+    (2, 150, 20, 4, 128, "bf16"),    # n_rep = 5: second quad has 3 padding slots
+    (1, 200, 48, 8, 64, "bf16"),     # n_rep = 6 at d = 64
+    (1, 120, 28, 4, 128, "f16"),     # n_rep = 7
     (1, 1, 8, 2, 128, "bf16"),       # single position
     (2, 100, 8, 2, 64, "f32"),
     (1, 70, 16, 16, 128, "f32"),
