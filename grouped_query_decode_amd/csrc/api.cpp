@@ -102,6 +102,11 @@ size_t workspace_for(int B, int H, int d, int S) {
 }
 
 gqa_status launched(hipError_t e, const char* what) {
+  if (e == gqa::kAbiMismatch)
+    return fail(GQA_ERR_LAUNCH,
+                "%s: launch refused: the kernel object and the API object of this library were "
+                "built from different versions of the argument structures (rebuild libgqa.so)",
+                what);
   if (e != hipSuccess)
     return fail(GQA_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
   return ok();
@@ -174,7 +179,7 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
   if (!gqkva && n_rep > 16 && n_rep % 16 == 0 && int64_t(B) * G * (n_rep / 16) <= kMaxCountedUnits)
     kv_div = n_rep / 16;
   if (dtype != GQA_DTYPE_F32 && gqa::decode_mfma_supports(n_rep / kv_div, d, S, split_len)) {
-    gqa::DecodeProblem p{};
+    auto p = gqa::problem_for<gqa::DecodeProblem>();
     p.q = static_cast<const uint16_t*>(q);
     p.k = static_cast<const uint16_t*>(k);
     p.v = static_cast<const uint16_t*>(v);
@@ -198,14 +203,14 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
   } else {
     if (append && n_max > 0) {
       // float32 path: the new rows go in first (same stream, so the decode sees them)
-      gqa::AppendProblem a{};
+      auto a = gqa::problem_for<gqa::AppendProblem>();
       a.k_new = k_new; a.v_new = v_new; a.k = const_cast<void*>(k); a.v = const_cast<void*>(v);
       a.seqlens = seqlens; a.B = B; a.G = G; a.n_max = n_max;
       a.row_bytes = d * (dtype == GQA_DTYPE_F32 ? 4 : 2);
       gqa_status st = launched(gqa::launch_append(a, stream), "gqa_decode_append (append)");
       if (st != GQA_OK) return st;
     }
-    gqa::RowsProblem p{};
+    auto p = gqa::problem_for<gqa::RowsProblem>();
     p.q = q; p.k = k; p.v = v; p.seqlens = seqlens; p.out = out;
     p.part_o = part_o; p.part_ml = part_ml;
     p.n_rows = B; p.rows_per_batch = 1;
@@ -223,7 +228,7 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
     if (st != GQA_OK) return st;
   }
   if (S > 1) {
-    gqa::CombineProblem c{};
+    auto c = gqa::problem_for<gqa::CombineProblem>();
     c.part_o = part_o; c.part_ml = part_ml; c.out = out;
     c.n_rows = B; c.H = Hp; c.d = d; c.num_splits = S; c.dtype = dtype;
     c.n_rep = n_rep; c.hm = hm;
@@ -269,7 +274,7 @@ gqa_status prefill_impl(const char* name, const void* q, const void* k, const vo
   const int64_t kv_p = cache_layout ? d : int64_t(G) * d;
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
   if (dtype != GQA_DTYPE_F32 && gqa::prefill_mfma_supports(n_rep, d, kv_cap, kv_p)) {
-    gqa::PrefillProblem p{};
+    auto p = gqa::problem_for<gqa::PrefillProblem>();
     p.q = static_cast<const uint16_t*>(q);
     p.k = static_cast<const uint16_t*>(k);
     p.v = static_cast<const uint16_t*>(v);
@@ -283,7 +288,7 @@ gqa_status prefill_impl(const char* name, const void* q, const void* k, const vo
     p.scale = scale;
     return launched(gqa::launch_prefill_mfma(p, stream), name);
   }
-  gqa::RowsProblem p{};
+  auto p = gqa::problem_for<gqa::RowsProblem>();
   p.q = q; p.k = k; p.v = v; p.seqlens = nullptr; p.out = out;
   p.n_rows = B * T; p.rows_per_batch = T;
   p.H = int(out_heads); p.G = G; p.n_rep = n_rep; p.d = d;
@@ -321,7 +326,7 @@ size_t gqa_decode_workspace_bytes(int B, int H, int G, int d, int n_max, int num
 
 gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* seqlens, void* out, int B, int H, int G, int d, int n_max,
-                      float scale, int dtype, void* workspace, size_t workspace_bytes,
+                      float scale, gqa_dtype dtype, void* workspace, size_t workspace_bytes,
                       void* stream) {
   return decode_impl(q, k_cache, v_cache, seqlens, out, B, H, G, d, n_max, scale, dtype, 0,
                      workspace, workspace_bytes, stream);
@@ -329,7 +334,7 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
 
 gqa_status gqa_decode_split(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* seqlens, void* out, int B, int H, int G, int d,
-                            int n_max, float scale, int dtype, int num_splits, void* workspace,
+                            int n_max, float scale, gqa_dtype dtype, int num_splits, void* workspace,
                             size_t workspace_bytes, void* stream) {
   return decode_impl(q, k_cache, v_cache, seqlens, out, B, H, G, d, n_max, scale, dtype,
                      num_splits, workspace, workspace_bytes, stream);
@@ -337,7 +342,7 @@ gqa_status gqa_decode_split(const void* q, const void* k_cache, const void* v_ca
 
 gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
                              void* v_cache, const int32_t* seqlens, void* out, int B, int H, int G,
-                             int d, int n_max, float scale, int dtype, int num_splits,
+                             int d, int n_max, float scale, gqa_dtype dtype, int num_splits,
                              void* workspace, size_t workspace_bytes, void* stream) {
   if (B > 0 && (!k_new || !v_new)) {
     g_last_error.clear();
@@ -348,20 +353,20 @@ gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new
 }
 
 gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void* out, int B,
-                              int T, int H, int G, int d, float scale, int dtype, void* stream) {
+                              int T, int H, int G, int d, float scale, gqa_dtype dtype, void* stream) {
   return prefill_impl("gqa_prefill_causal", q, k, v, out, nullptr, false, B, T, H, G, d, 0, scale,
                       dtype, stream, false);
 }
 
 gqa_status gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* ctx_lens, void* out, int B, int T, int H, int G, int d,
-                             int n_max, float scale, int dtype, void* stream) {
+                             int n_max, float scale, gqa_dtype dtype, void* stream) {
   return prefill_impl("gqa_prefill_chunk", q, k_cache, v_cache, out, ctx_lens, true, B, T, H, G, d,
                       n_max, scale, dtype, stream, false);
 }
 
 gqa_status gqkva_prefill_causal(const void* q, const void* k, const void* v, void* out, int B,
-                                int T, int g_q, int g_kv, int d, float scale, int dtype,
+                                int T, int g_q, int g_kv, int d, float scale, gqa_dtype dtype,
                                 void* stream) {
   return prefill_impl("gqkva_prefill_causal", q, k, v, out, nullptr, false, B, T, g_q, g_kv, d, 0,
                       scale, dtype, stream, true);
@@ -369,7 +374,7 @@ gqa_status gqkva_prefill_causal(const void* q, const void* k, const void* v, voi
 
 gqa_status gqkva_decode(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* seqlens, void* out, int B, int g_q, int g_kv, int d,
-                        int n_max, float scale, int dtype, int num_splits, void* workspace,
+                        int n_max, float scale, gqa_dtype dtype, int num_splits, void* workspace,
                         size_t workspace_bytes, void* stream) {
   return decode_impl(q, k_cache, v_cache, seqlens, out, B, g_q, g_kv, d, n_max, scale, dtype,
                      num_splits, workspace, workspace_bytes, stream, nullptr, nullptr, true);
@@ -384,7 +389,7 @@ size_t gqkva_decode_workspace_bytes(int B, int g_q, int g_kv, int d, int n_max, 
 }
 
 gqa_status kv_meanpool_heads(const void* w_in, void* w_out, int H, int G, int64_t per_head_elems,
-                             int dtype, void* stream_v) {
+                             gqa_dtype dtype, void* stream_v) {
   g_last_error.clear();
   if (!known_dtype(dtype))
     return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: unknown dtype %d", dtype);
@@ -400,7 +405,7 @@ gqa_status kv_meanpool_heads(const void* w_in, void* w_out, int H, int G, int64_
     return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: tensors must be 16-byte aligned");
   if (int64_t(H) * per_head_elems > (int64_t(1) << 40))
     return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: problem too large");
-  gqa::MeanpoolProblem p{};
+  auto p = gqa::problem_for<gqa::MeanpoolProblem>();
   p.w_in = w_in; p.w_out = w_out; p.H = H; p.G = G; p.n_rep = H / G;
   p.per_head_elems = per_head_elems; p.dtype = dtype;
   return launched(gqa::launch_meanpool(p, static_cast<hipStream_t>(stream_v)),

@@ -31,6 +31,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendProblem p) {
 }  // namespace
 
 hipError_t launch_append(const AppendProblem& p, hipStream_t stream) {
+  if (!abi_ok(p)) return kAbiMismatch;
   const int64_t units = int64_t(p.B) * p.G;
   if (units <= 0) return hipSuccess;
   const unsigned blocks = unsigned(units < 65536 ? units : 65536);

@@ -52,6 +52,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineProblem p) {
 }  // namespace
 
 hipError_t launch_combine(const CombineProblem& p, hipStream_t stream) {
+  if (!abi_ok(p)) return kAbiMismatch;
   const int64_t pairs = int64_t(p.n_rows) * p.H;
   const int64_t blocks = (pairs + 3) / 4;
   if (blocks <= 0) return hipSuccess;

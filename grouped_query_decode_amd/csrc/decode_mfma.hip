@@ -513,6 +513,7 @@ hipError_t launch_dt(const DecodeProblem& p, hipStream_t stream) {
 }
 
 hipError_t launch_decode_mfma(const DecodeProblem& p, hipStream_t stream) {
+  if (!abi_ok(p)) return kAbiMismatch;
   return p.dtype == kF16 ? launch_dt<kF16>(p, stream) : launch_dt<kBF16>(p, stream);
 }
 

@@ -6,6 +6,26 @@
 
 namespace gqa {
 
+// Every problem structure below starts with abi_bytes, the structure's size as
+// the code that filled it in saw it; each launcher compares that with its own
+// sizeof and refuses the launch (kAbiMismatch, before any HIP call) when they
+// differ.  Kernel files and the C-ABI layer are separate objects: a library
+// linked from objects built against different versions of this header would
+// otherwise hand a kernel shifted arguments.
+constexpr hipError_t kAbiMismatch = hipErrorInvalidKernelFile;
+
+template <class P>
+inline P problem_for() {
+  P p{};
+  p.abi_bytes = uint32_t(sizeof(P));
+  return p;
+}
+
+template <class P>
+inline bool abi_ok(const P& p) {
+  return p.abi_bytes == uint32_t(sizeof(P));
+}
+
 enum Dtype { kF32 = 0, kBF16 = 1, kF16 = 2 };
 
 // Which query row feeds, and which output row receives, query r (0 .. n_rep-1)
@@ -29,6 +49,7 @@ inline HeadMap gqkva_head_map(int g_q, int g_kv) {
 // kernel for decode (one row per sequence) and for float32 causal prefill (one
 // row per prompt position).  All strides are in elements.
 struct RowsProblem {
+  uint32_t abi_bytes;        // sizeof(RowsProblem) where it was filled in (see problem_for)
   const void* q;
   const void* k;
   const void* v;
@@ -53,6 +74,7 @@ struct RowsProblem {
 
 // Batched decode on the matrix cores (bf16 only).
 struct DecodeProblem {
+  uint32_t abi_bytes;        // sizeof(DecodeProblem) where it was filled in (see problem_for)
   const uint16_t* q;        // [B, H, d]
   const uint16_t* k;        // [B, G, n_max, d]
   const uint16_t* v;
@@ -75,6 +97,7 @@ struct DecodeProblem {
 };
 
 struct CombineProblem {
+  uint32_t abi_bytes;        // sizeof(CombineProblem) where it was filled in (see problem_for)
   const float* part_o;
   const float* part_ml;
   void* out;                // rows of hm.o_heads*d elements, in dtype
@@ -88,6 +111,7 @@ struct CombineProblem {
 // of sequence b sits at position ctx_b + t (ctx_b = ctx_lens[b], or 0) and
 // attends positions 0 .. min(ctx_b + t, kv_cap - 1) of its K/V head.
 struct PrefillProblem {
+  uint32_t abi_bytes;        // sizeof(PrefillProblem) where it was filled in (see problem_for)
   const uint16_t* q;        // [B, T, hm.q_heads, d]
   const uint16_t* k;        // position j of (b, g) at b*kv_bstride + g*kv_gstride + j*kv_pstride
   const uint16_t* v;
@@ -104,6 +128,7 @@ struct PrefillProblem {
 // Write this step's k, v rows into the caches at position seqlens[b]-1
 // (when 1 <= seqlens[b] <= n_max), any element type.
 struct AppendProblem {
+  uint32_t abi_bytes;        // sizeof(AppendProblem) where it was filled in (see problem_for)
   const void* k_new;        // [B, G, row_bytes]
   const void* v_new;
   void* k;                  // [B, G, n_max, row_bytes]
@@ -114,6 +139,7 @@ struct AppendProblem {
 };
 
 struct MeanpoolProblem {
+  uint32_t abi_bytes;        // sizeof(MeanpoolProblem) where it was filled in (see problem_for)
   const void* w_in;
   void* w_out;
   int H, G, n_rep;

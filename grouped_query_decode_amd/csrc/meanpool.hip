@@ -116,6 +116,7 @@ __global__ __launch_bounds__(256) void meanpool_scalar_kernel(MeanpoolProblem p)
 }  // namespace
 
 hipError_t launch_meanpool(const MeanpoolProblem& p, hipStream_t stream) {
+  if (!abi_ok(p)) return kAbiMismatch;
   const bool vec = (p.per_head_elems % 8) == 0;
   const int64_t work = vec ? int64_t(p.G) * (p.per_head_elems / 8) : int64_t(p.G) * p.per_head_elems;
   // enough threads to cover the output once, capped (grid-stride beyond)

@@ -464,6 +464,7 @@ hipError_t launch_d(const PrefillProblem& p, hipStream_t stream) {
 }
 
 hipError_t launch_prefill_mfma(const PrefillProblem& p, hipStream_t stream) {
+  if (!abi_ok(p)) return kAbiMismatch;
   // d = 128: 8 waves (one workgroup per CU, by registers).  d = 64: 4 waves,
   // two workgroups per CU -- one's start and end overlap the other's tiles
   // (measured 3% faster than 8 waves at d = 64; at d = 128, 4 waves spill).

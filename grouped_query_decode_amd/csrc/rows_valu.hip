@@ -244,6 +244,7 @@ hipError_t launch_t(const RowsProblem& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_rows_valu(const RowsProblem& p, int dtype, hipStream_t stream) {
+  if (!abi_ok(p)) return kAbiMismatch;
   if (dtype == kF32) {
     return p.d == 64 ? launch_t<kF32, 64>(p, stream) : launch_t<kF32, 128>(p, stream);
   }

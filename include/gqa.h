@@ -40,18 +40,24 @@
 extern "C" {
 #endif
 
-enum {
-  GQA_DTYPE_F32 = 0,
-  GQA_DTYPE_BF16 = 1,
-  GQA_DTYPE_F16 = 2
-};
+/* Element type of every tensor argument of a call (inputs and outputs share
+ * it).  Passed by value; an int-sized enum, so callers through a plain C FFI
+ * may pass the int codes. */
+typedef enum gqa_dtype {
+  GQA_DTYPE_F32 = 0,         /* float                                          */
+  GQA_DTYPE_BF16 = 1,        /* bfloat16 (top half of a float, round to even)  */
+  GQA_DTYPE_F16 = 2          /* IEEE 754 binary16                              */
+} gqa_dtype;
 
 typedef enum gqa_status {
   GQA_OK = 0,
   GQA_ERR_INVALID_ARG = 1,   /* shapes, pointers, alignment, scale, H % G != 0   */
   GQA_ERR_UNSUPPORTED = 2,   /* valid, but not built: head size other than 64/128 */
   GQA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required        */
-  GQA_ERR_LAUNCH = 4         /* the HIP runtime refused a kernel launch            */
+  GQA_ERR_LAUNCH = 4         /* the HIP runtime refused a kernel launch, or the
+                                library's own objects disagree on the size of an
+                                internal argument structure (a build from mixed
+                                sources); nothing is enqueued in the latter case */
 } gqa_status;
 
 /*
@@ -120,7 +126,7 @@ size_t gqa_decode_workspace_bytes(int B, int H, int G, int d, int n_max, int num
  */
 gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* seqlens, void* out,
-                      int B, int H, int G, int d, int n_max, float scale, int dtype,
+                      int B, int H, int G, int d, int n_max, float scale, gqa_dtype dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -131,7 +137,7 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
  */
 gqa_status gqa_decode_split(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* seqlens, void* out,
-                            int B, int H, int G, int d, int n_max, float scale, int dtype,
+                            int B, int H, int G, int d, int n_max, float scale, gqa_dtype dtype,
                             int num_splits, void* workspace, size_t workspace_bytes,
                             void* stream);
 
@@ -162,7 +168,7 @@ gqa_status gqa_decode_split(const void* q, const void* k_cache, const void* v_ca
  */
 gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new,
                              void* k_cache, void* v_cache, const int32_t* seqlens, void* out,
-                             int B, int H, int G, int d, int n_max, float scale, int dtype,
+                             int B, int H, int G, int d, int n_max, float scale, gqa_dtype dtype,
                              int num_splits, void* workspace, size_t workspace_bytes,
                              void* stream);
 
@@ -188,7 +194,7 @@ gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new
  * runs on the vector units in float32.  Errors as for gqa_decode; B = 0 or T = 0 is a valid no-op.
  */
 gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void* out,
-                              int B, int T, int H, int G, int d, float scale, int dtype,
+                              int B, int T, int H, int G, int d, float scale, gqa_dtype dtype,
                               void* stream);
 
 /*
@@ -218,7 +224,7 @@ gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void*
  */
 gqa_status gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* ctx_lens, void* out,
-                             int B, int T, int H, int G, int d, int n_max, float scale, int dtype,
+                             int B, int T, int H, int G, int d, int n_max, float scale, gqa_dtype dtype,
                              void* stream);
 
 /*
@@ -240,11 +246,11 @@ gqa_status gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_c
  */
 gqa_status gqkva_decode(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* seqlens, void* out,
-                        int B, int g_q, int g_kv, int d, int n_max, float scale, int dtype,
+                        int B, int g_q, int g_kv, int d, int n_max, float scale, gqa_dtype dtype,
                         int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 size_t gqkva_decode_workspace_bytes(int B, int g_q, int g_kv, int d, int n_max, int num_splits);
 gqa_status gqkva_prefill_causal(const void* q, const void* k, const void* v, void* out,
-                                int B, int T, int g_q, int g_kv, int d, float scale, int dtype,
+                                int B, int T, int g_q, int g_kv, int d, float scale, gqa_dtype dtype,
                                 void* stream);
 
 /*
@@ -267,7 +273,7 @@ gqa_status gqkva_prefill_causal(const void* q, const void* k, const void* v, voi
  * per_head_elems = 0 is a valid no-op.
  */
 gqa_status kv_meanpool_heads(const void* w_in, void* w_out, int H, int G,
-                             int64_t per_head_elems, int dtype, void* stream);
+                             int64_t per_head_elems, gqa_dtype dtype, void* stream);
 
 /* Static text for a status code ("GQA_OK", ...); never NULL. */
 const char* gqa_status_string(int status);

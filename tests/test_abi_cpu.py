@@ -266,3 +266,55 @@ def test_plain_c_consumer(tmp_path, lib):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
     assert "splits=" in r.stdout
+
+
+ABI_MAIN = r"""
+#include "internal.h"
+#include <cstdio>
+int main(int argc, char**) {
+  // an empty decode problem (B = 0) launches nothing once the check passes
+  auto d = gqa::problem_for<gqa::DecodeProblem>();
+  const hipError_t ed = gqa::launch_decode_mfma(d, nullptr);
+  hipError_t ep = hipSuccess;
+  if (argc > 1) {      // only with a mis-sized structure: refused before use
+    auto p = gqa::problem_for<gqa::PrefillProblem>();
+    ep = gqa::launch_prefill_mfma(p, nullptr);
+  }
+  std::printf("decode=%d prefill=%d\n", int(ed), int(ep));
+  return (ed == gqa::kAbiMismatch && ep == gqa::kAbiMismatch) ? 0 : 1;
+}
+"""
+
+
+@pytest.mark.parametrize("stale", [False, True])
+def test_kernel_launchers_refuse_a_stale_argument_structure(tmp_path, lib, stale):
+    """A program built against a copy of the internal header whose decode and
+    prefill argument structures gained a field (as a stale or newer copy would)
+    hands the library's launchers structures of the wrong size: they must
+    refuse before any HIP call (this runs without a GPU).  With the header as
+    shipped the same program's empty decode problem passes the check and
+    launches nothing."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("no C++ compiler or ROCm headers")
+    text = open(os.path.join(ROOT, "grouped_query_decode_amd", "csrc", "internal.h")).read()
+    if stale:
+        for anchor in ("  int dtype;                // kBF16 or kF16\n  HeadMap hm;\n  // G work",
+                       "  const int32_t* ctx_lens;  // [B] or null\n"):
+            assert text.count(anchor) == 1, anchor
+            text = text.replace(anchor, "  const void* extra_field;\n" + anchor)
+    (tmp_path / "internal.h").write_text(text)
+    (tmp_path / "main.cpp").write_text(ABI_MAIN)
+    exe = tmp_path / "abi_main"
+    libdir = os.path.dirname(gqa.library_path())
+    subprocess.run([gxx, "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    "-I", str(tmp_path), str(tmp_path / "main.cpp"), "-o", str(exe), "-L", libdir,
+                    "-lgqa", f"-Wl,-rpath,{libdir}"], check=True)
+    r = subprocess.run([str(exe)] + (["both"] if stale else []), capture_output=True, text=True,
+                       timeout=60)
+    if stale:
+        assert r.returncode == 0, (r.stdout, r.stderr)
+    else:
+        assert r.returncode == 1 and r.stdout.strip() == "decode=0 prefill=0", (r.stdout, r.stderr)
