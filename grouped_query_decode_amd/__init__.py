@@ -8,6 +8,7 @@ library is missing, every call raises.
 
     decode(q, k_cache, v_cache, seqlens)        # one decode step, [B,H,d]
     decode_append(q, k_new, v_new, k_cache, v_cache, seqlens)  # append, then decode
+    decode_noalloc(q, k_cache, v_cache, seqlens)  # decode with the library's static scratch
     prefill_causal(q, k, v)                     # causal prefill, [B,T,H,d]
     prefill_chunk(q, k_cache, v_cache, ctx_lens) # a prompt chunk after ctx cached positions
     gqkva_decode(q, k_cache, v_cache, seqlens)  # all query-group x K/V-group pairs
@@ -24,7 +25,8 @@ import os
 import torch
 
 __all__ = [
-    "GQAError", "library_path", "load_library", "decode", "decode_append", "decode_num_splits",
+    "GQAError", "library_path", "load_library", "decode", "decode_append", "decode_noalloc",
+    "decode_num_splits",
     "decode_workspace_bytes", "prefill_causal", "prefill_chunk", "gqkva_decode",
     "gqkva_prefill_causal", "meanpool_heads", "DTYPE_CODES",
 ]
@@ -74,6 +76,8 @@ def load_library():
     lib.gqa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                       i32, vp, sz, vp]
     lib.gqa_decode_append.restype = i32
+    lib.gqa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+    lib.gqa_decode_noalloc.restype = i32
     lib.gqa_prefill_causal.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.gqa_prefill_causal.restype = i32
     lib.gqa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
@@ -194,6 +198,39 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlen
                               B, H, G, d, n_max, float(scale), _dtype_code(q), int(num_splits),
                               _ptr(workspace), ws_bytes, ctypes.c_void_p(_stream_handle(dev)))
     _check("gqa_decode", st)
+    return out
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   seqlens: torch.Tensor, out: torch.Tensor, scale: float | None = None,
+                   num_splits: int = 0) -> torch.Tensor:
+    """:func:`decode` through ``gqa_decode_noalloc``: the split partials live in
+    the library's static per-GPU scratch, so the call allocates nothing (``out``
+    must be given).  Calls that may overlap on one GPU race on that scratch."""
+    lib = load_library()
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B,H,d] and k_cache [B,G,Nmax,d]")
+    B, H, d = q.shape
+    Bk, G, n_max, dk = k_cache.shape
+    if (Bk, dk) != (B, d) or v_cache.shape != k_cache.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k_cache.shape)}, "
+                         f"v {tuple(v_cache.shape)}")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    if seqlens.dtype != torch.int32 or seqlens.shape != (B,):
+        raise ValueError("seqlens must be an int32 tensor of shape [B]")
+    dev = q.device
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seqlens", seqlens),
+                    ("out", out)):
+        _require_device(name, t, dev)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.gqa_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(out),
+                                B, H, G, d, n_max, float(scale), _dtype_code(q), int(num_splits),
+                                ctypes.c_void_p(_stream_handle(dev)))
+    _check("gqa_decode_noalloc", st)
     return out
 
 

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/gqa.h"
@@ -118,7 +119,7 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
                        void* out, int B, int H, int G, int d, int n_max, float scale, int dtype,
                        int num_splits, void* ws, size_t ws_bytes, void* stream_v,
                        const void* k_new = nullptr, const void* v_new = nullptr,
-                       bool gqkva = false) {
+                       bool gqkva = false, bool check_only = false) {
   g_last_error.clear();
   const bool append = k_new != nullptr || v_new != nullptr;
   if (!known_dtype(dtype)) return fail(GQA_ERR_INVALID_ARG, "gqa_decode: unknown dtype %d", dtype);
@@ -158,6 +159,8 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
   if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned16(ws)))
     return fail(GQA_ERR_WORKSPACE, "gqa_decode: workspace of %zu bytes needed, %zu given%s", need,
                 ws_bytes, (ws && !aligned16(ws)) ? " (misaligned)" : "");
+
+  if (check_only) return ok();
 
   float* part_o = nullptr;
   float* part_ml = nullptr;
@@ -305,6 +308,57 @@ gqa_status prefill_impl(const char* name, const void* q, const void* k, const vo
   return launched(gqa::launch_rows_valu(p, dtype, stream), name);
 }
 
+// ---------------------------------------------------------------------------
+// Decode without allocation: the split workspace lives in a static device
+// array (one copy per GPU, held until the process ends) instead of a caller
+// buffer.  In host code `scratch` names a host-side stand-in, never the device
+// memory: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is passed on.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = GQA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// Clears the split-arrival counters (an ordinary kernel: safe under graph
+// capture, unlike a memset node).
+__global__ void clear_counters_kernel(int* counters, int n) {
+  for (int i = int(blockIdx.x * blockDim.x + threadIdx.x); i < n; i += int(gridDim.x * blockDim.x))
+    counters[i] = 0;
+}
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device (set up on the first call
+// there: the lookup, then a clear of the counter header enqueued on `stream`,
+// ahead of that call's kernels; static storage also starts zeroed).
+gqa_status scratch_for_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GQA_ERR_LAUNCH, "gqa_decode_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GQA_ERR_UNSUPPORTED, "gqa_decode_noalloc: device %d (at most %d devices)", dev, kMaxDevices);
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&] {
+    void* ptr = nullptr;
+    slot.err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (slot.err != hipSuccess) return;
+    hipLaunchKernelGGL(clear_counters_kernel, dim3(16), dim3(256), 0, stream, static_cast<int*>(ptr),
+                       int(kCounterBytes / sizeof(int)));
+    slot.err = hipGetLastError();
+    if (slot.err == hipSuccess) slot.ptr = ptr;
+  });
+  if (slot.err != hipSuccess || slot.ptr == nullptr)
+    return fail(GQA_ERR_LAUNCH, "gqa_decode_noalloc: static scratch set-up on device %d failed: %s", dev,
+                hipGetErrorString(slot.err));
+  *out = slot.ptr;
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -426,5 +480,40 @@ const char* gqa_status_string(int status) {
 const char* gqa_last_error(void) { return g_last_error.c_str(); }
 
 int gqa_version(void) { return 100; }
+
+gqa_status gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* seqlens, void* out, int B, int H, int G, int d,
+                              int n_max, float scale, gqa_dtype dtype, int num_splits,
+                              void* stream) {
+  g_last_error.clear();
+  if (!decode_shape_valid(B, H, G, d, n_max) || num_splits < 0)
+    // the full argument checks (with their messages) are decode_impl's
+    return decode_impl(q, k_cache, v_cache, seqlens, out, B, H, G, d, n_max, scale, dtype,
+                       num_splits, nullptr, 0, stream);
+  int S_req = B == 0 ? 1
+                     : (num_splits == 0 ? plan_splits(B, G, n_max)
+                                        : std::min(num_splits, std::max(n_max, 1)));
+  int S, len;
+  split_geometry(n_max, S_req, &S, &len);
+  const size_t need = workspace_for(B, H, d, S);
+  if (need > kScratchBytes)
+    return fail(GQA_ERR_WORKSPACE,
+                "gqa_decode_noalloc: this shape needs %zu bytes of split scratch (B=%d, H=%d, d=%d, "
+                "%d splits); the static scratch holds %zu (GQA_NOALLOC_SCRATCH_BYTES): use "
+                "gqa_decode_split with a workspace, or fewer splits",
+                need, B, H, d, S, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    // argument errors first, so that an invalid call makes no HIP call
+    gqa_status st = decode_impl(q, k_cache, v_cache, seqlens, out, B, H, G, d, n_max, scale,
+                                dtype, num_splits, reinterpret_cast<void*>(uintptr_t(256)),
+                                kScratchBytes, stream, nullptr, nullptr, false, /*check_only=*/true);
+    if (st != GQA_OK) return st;
+    st = scratch_for_current_device(static_cast<hipStream_t>(stream), &ws);
+    if (st != GQA_OK) return st;
+  }
+  return decode_impl(q, k_cache, v_cache, seqlens, out, B, H, G, d, n_max, scale, dtype,
+                     num_splits, ws, need > 0 ? kScratchBytes : 0, stream);
+}
 
 }  // extern "C"

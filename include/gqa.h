@@ -275,6 +275,37 @@ gqa_status gqkva_prefill_causal(const void* q, const void* k, const void* v, voi
 gqa_status kv_meanpool_heads(const void* w_in, void* w_out, int H, int G,
                              int64_t per_head_elems, gqa_dtype dtype, void* stream);
 
+/*
+ * gqa_decode_noalloc - gqa_decode_split for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation, kernels and results, with the
+ * split partials and arrival counters in a static device array of
+ * GQA_NOALLOC_SCRATCH_BYTES inside the library instead of a caller workspace.
+ *
+ * The caller still passes every input and output (same meaning, layout and
+ * checks as gqa_decode_split).  The call itself allocates nothing
+ * (no hipMalloc/hipFree or allocating library routine).  The array exists once
+ * per GPU the library runs on, for the life of the process; the first call on
+ * a device looks up its address there (hipGetSymbolAddress, on the current
+ * device: `stream` must belong to it) and enqueues one small kernel on
+ * `stream` that clears the counter header.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that may overlap in time on one GPU (other streams, other
+ * threads) RACE and must be serialised by the caller.
+ *
+ * Errors: as gqa_decode_split; GQA_ERR_WORKSPACE when the shape's split
+ * partials (gqa_decode_workspace_bytes with the same arguments) exceed
+ * GQA_NOALLOC_SCRATCH_BYTES -- e.g. the planner's split of 64 sequences x 32
+ * heads x d=128 over 32768 positions needs about 17 MB and fits; lower
+ * num_splits to fit larger batches.  GQA_ERR_LAUNCH if the set-up fails.
+ */
+#define GQA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+gqa_status gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* seqlens, void* out,
+                              int B, int H, int G, int d, int n_max, float scale, gqa_dtype dtype,
+                              int num_splits, void* stream);
+
 /* Static text for a status code ("GQA_OK", ...); never NULL. */
 const char* gqa_status_string(int status);
 

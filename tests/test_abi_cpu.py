@@ -38,7 +38,7 @@ def test_header_declares_the_api():
               "gqa_prefill_chunk", "gqkva_decode", "gqkva_decode_workspace_bytes",
               "gqkva_prefill_causal", "kv_meanpool_heads",
               "gqa_decode_workspace_bytes", "gqa_decode_num_splits", "gqa_status_string",
-              "gqa_last_error", "gqa_version"):
+              "gqa_last_error", "gqa_version", "gqa_decode_noalloc"):
         assert n in names, n
 
 
@@ -318,3 +318,23 @@ def test_kernel_launchers_refuse_a_stale_argument_structure(tmp_path, lib, stale
         assert r.returncode == 0, (r.stdout, r.stderr)
     else:
         assert r.returncode == 1 and r.stdout.strip() == "decode=0 prefill=0", (r.stdout, r.stderr)
+
+
+def test_decode_noalloc_host_checks(lib):
+    """gqa_decode_noalloc rejects invalid arguments and shapes whose split
+    partials exceed its static scratch on the host, before any HIP call."""
+    def call(B=2, H=8, G=2, d=64, n=128, splits=0, q=P, sl=P, dt=BF16):
+        return lib.gqa_decode_noalloc(q, P, P, sl, P, B, H, G, d, n, 0.125, dt, splits, None)
+    assert call(H=6, G=4) == INVALID
+    assert call(q=ctypes.c_void_p(0)) == INVALID
+    assert call(sl=ctypes.c_void_p(0)) == INVALID
+    assert call(q=P_MIS) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(dt=9) == INVALID
+    assert call(splits=-1) == INVALID
+    assert call(B=0) == OK
+    # 64 sequences x 1024 heads x d=128 in 16 splits: ~537 MB of partials
+    assert call(B=64, H=1024, G=1, d=128, n=4096, splits=16) == WORKSPACE
+    assert "static scratch" in lib.gqa_last_error().decode()
+    need = lib.gqa_decode_workspace_bytes(64, 32, 8, 128, 32768, 0)
+    assert 0 < need <= 32 << 20          # the ragged 32k workload fits
