@@ -1,0 +1,64 @@
+// Achievable HBM read bandwidth on gfx950, for the benchmark's ceiling: every
+// lane streams 16-byte loads with the non-temporal hint (the data is read
+// once and should not displace cached lines), U loads in flight per lane per
+// iteration, over a buffer much larger than the 256 MB last-level cache.  The
+// loaded words are folded into one value that is stored only if it equals an
+// impossible key, so no load can be optimised away and almost nothing is
+// written.  This is measurement code, separate from libgqa.so.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../../include/gqa_probe.h"
+
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kThreads = 256;
+
+template <int U>
+__global__ __launch_bounds__(kThreads) void hbm_read_probe_kernel(const u32x4_t* __restrict__ p, int64_t n16,
+                                                                  uint32_t* sink, uint32_t key) {
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  const int64_t stride = int64_t(gridDim.x) * kThreads * U;
+  int64_t i = int64_t(blockIdx.x) * kThreads * U + threadIdx.x;
+  // whole chunks: this lane's U elements i, i + 256, ..., i + 256 (U - 1) are all below n16
+  for (; i + int64_t(U - 1) * kThreads < n16; i += stride) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + i + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u];
+  }
+  // the one partial chunk left, element by element
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (i + int64_t(u) * kThreads < n16) acc ^= __builtin_nontemporal_load(p + i + u * kThreads);
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == key) sink[0] = 1u;
+}
+
+template <int U>
+hipError_t launch(const void* buf, int64_t n16, uint32_t* sink, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL((hbm_read_probe_kernel<U>), dim3(unsigned(blocks)), dim3(kThreads), 0, s,
+                     static_cast<const u32x4_t*>(buf), n16, sink, 0x9e3779b9u);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" int gqa_probe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, int unroll,
+                                  void* stream) {
+  if (!buf || !sink || bytes == 0 || (bytes & 15u) || (reinterpret_cast<uintptr_t>(buf) & 15u) ||
+      (reinterpret_cast<uintptr_t>(sink) & 3u) || blocks < 1 || blocks > (1 << 20))
+    return 1;
+  const int64_t n16 = int64_t(bytes / 16);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (unroll) {
+    case 4: e = launch<4>(buf, n16, sink, blocks, s); break;
+    case 8: e = launch<8>(buf, n16, sink, blocks, s); break;
+    case 16: e = launch<16>(buf, n16, sink, blocks, s); break;
+    default: return 1;
+  }
+  return e == hipSuccess ? 0 : 4;
+}

@@ -1,0 +1,37 @@
+/*
+ * gqa_probe.h - C ABI of libgqa_probe.so: measurement probes for the
+ * benchmark (not part of the attention library).
+ *
+ * gqa_probe_hbm_read - read `bytes` of device memory once with 16-byte
+ * non-temporal loads (every lane keeps `unroll` loads in flight, `blocks`
+ * workgroups of 256 threads stride over the buffer) and fold them into one
+ * value that is written to sink[0] only if it equals a fixed key.  Timing
+ * calls over a buffer much larger than the 256 MB last-level cache gives the
+ * HBM read rate a streaming kernel can reach: the measured ceiling against
+ * which the memory-bound kernels are also reported.
+ *
+ *   buf     device pointer, 16-byte aligned; bytes a positive multiple of 16.
+ *   sink    device pointer to at least 4 writable bytes.
+ *   blocks  1 .. 2^20;  unroll  4, 8 or 16.
+ *   stream  hipStream_t as void* (enqueued asynchronously).
+ * Returns 0, 1 for an invalid argument (nothing enqueued), 4 if the launch
+ * was refused.
+ */
+#ifndef GQA_PROBE_H_
+#define GQA_PROBE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+int gqa_probe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, int unroll,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_PROBE_H_ */

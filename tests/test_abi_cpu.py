@@ -18,8 +18,8 @@ P = ctypes.c_void_p(4096)        # aligned, non-null, never dereferenced on thes
 P_MIS = ctypes.c_void_p(4100)    # misaligned
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
     return sorted(set(names))
@@ -46,6 +46,28 @@ def test_library_exports_every_declared_symbol(lib):
     raw = ctypes.CDLL(gqa.library_path())
     for name in declared_functions():
         assert hasattr(raw, name), f"{name} declared in include/gqa.h but not exported"
+
+
+def test_probe_library_exports_its_header():
+    """The benchmark's measurement probes live in their own libgqa_probe.so."""
+    path = os.path.join(os.path.dirname(gqa.library_path()), "libgqa_probe.so")
+    if not os.path.exists(path):
+        pytest.fail("libgqa_probe.so is not built: run __graft_entry__.build() first")
+    raw = ctypes.CDLL(path)
+    names = declared_functions(os.path.join(ROOT, "include", "gqa_probe.h"))
+    assert names == ["gqa_probe_hbm_read"]
+    for name in names:
+        assert hasattr(raw, name)
+    f = raw.gqa_probe_hbm_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    # invalid arguments are refused on the host (nothing enqueued, no GPU needed)
+    assert f(P, 1 << 20, P, 1024, 3, None) == 1           # unroll
+    assert f(P, 1000, P, 1024, 8, None) == 1              # not a multiple of 16
+    assert f(P_MIS, 1 << 20, P, 1024, 8, None) == 1       # misaligned
+    assert f(ctypes.c_void_p(0), 1 << 20, P, 1024, 8, None) == 1
+    assert f(P, 1 << 20, P, 0, 8, None) == 1              # blocks
 
 
 def test_status_strings(lib):
