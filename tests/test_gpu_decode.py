@@ -279,18 +279,75 @@ def test_t5xxl_cross_attention_decode():
     assert_close(_run(x, scale), _oracle(x, scale), torch.bfloat16, "t5xxl")
 
 
-def test_ragged_long_context_decode():
+def _slice64(t):
+    """Exact float64 host copy of a (bf16 or f32) device slice (upcast on the GPU)."""
+    return t.double().cpu().numpy()
+
+
+def _oracle_all_sequences(x, scale):
+    """The oracle for every sequence, one sequence's attended cache rows at a time."""
+    sl = x["seqlens"].cpu().numpy()
+    n_max = x["k_cache"].shape[2]
+    outs = []
+    for b in range(x["q"].shape[0]):
+        n = max(oracle.attended_length(sl[b], n_max), 1)
+        outs.append(oracle.decode_ref(_slice64(x["q"][b:b + 1]), _slice64(x["k_cache"][b:b + 1, :, :n]),
+                                      _slice64(x["v_cache"][b:b + 1, :, :n]), [sl[b]], scale)[0])
+    return np.stack(outs)
+
+
+def test_ragged_long_context_decode_all_sequences():
+    """The ragged 32k workload at full size (B=64, H=32, G=8, d=128, lengths
+    uniform in [1, 32768], NaN beyond each length): every output row against
+    the oracle."""
     w = synth.WORKLOADS["ragged_longctx_decode_bf16"]
-    announce("decode ragged long context (8 GiB cache)")
+    announce("decode ragged long context (8 GiB cache), all 64 sequences")
     x = synth.decode_inputs(w.B, w.H, w.G, w.d, w.N, dtype="bf16", seed=w.seed, device=DEV,
                             seqlens="uniform", nan_tail=True)
     scale = synth.scale_for(w.d)
     out = _run(x, scale)
     assert torch.isfinite(out.float()).all()
-    sl = x["seqlens"].cpu().numpy()
-    rows = sorted({int(np.argmin(sl)), int(np.argmax(sl)), 0, 17, 33, 63})
-    ref = _oracle(x, scale, rows=rows)
-    assert_close(out[rows], ref, torch.bfloat16, "ragged long")
+    stats = assert_close(out, _oracle_all_sequences(x, scale), torch.bfloat16, "ragged long, all rows")
+    print(f"ragged long context, all {w.B} sequences: {stats}")
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_ragged_long_context_masking_is_bit_exact():
+    """At the ragged 32k workload's full size: the cache beyond each length
+    filled with NaN, then refilled in place with random values (and huge V),
+    then with a key at the first position past the length that would dominate
+    every score: the output bits must not change.  A dominant key at the last
+    attended position must take over (the length is not off by one)."""
+    w = synth.WORKLOADS["ragged_longctx_decode_bf16"]
+    announce("decode ragged long context masking bits (8 GiB cache)")
+    x = synth.decode_inputs(w.B, w.H, w.G, w.d, w.N, dtype="bf16", seed=w.seed, device=DEV,
+                            seqlens="uniform", nan_tail=True)
+    scale = synth.scale_for(w.d)
+    B, H, G, d, n_max = w.B, w.H, w.G, w.d, w.N
+    lens = x["seqlens"].cpu().tolist()
+    out_nan = _run(x, scale).clone()
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(123)
+    for b, n in enumerate(lens):
+        if n < n_max:
+            tail = x["k_cache"][b, :, n:]
+            tail.copy_(torch.randn(tail.shape, generator=gen, device=DEV).to(tail.dtype))
+            x["v_cache"][b, :, n:] = 1e4
+    out_rand = _run(x, scale).clone()
+    for b, n in enumerate(lens):
+        if n < n_max:
+            qg = x["q"][b].float().view(G, H // G, d).sum(1)
+            x["k_cache"][b, :, n] = (qg * 100).to(x["k_cache"].dtype)
+    out_dom = _run(x, scale).clone()
+    assert torch.equal(out_nan.view(torch.int16), out_rand.view(torch.int16))
+    assert torch.equal(out_nan.view(torch.int16), out_dom.view(torch.int16))
+    for b, n in enumerate(lens):
+        qg = x["q"][b].float().view(G, H // G, d).sum(1)
+        x["k_cache"][b, :, n - 1] = (qg * 100).to(x["k_cache"].dtype)
+        x["v_cache"][b, :, n - 1] = 2.0
+    out_last = _run(x, scale)
+    assert torch.equal(out_last, torch.full_like(out_last, 2.0))
     del x
     torch.cuda.empty_cache()
 
