@@ -140,8 +140,10 @@ def _eager_ms(torch, fn, n_calls):
     return a.elapsed_time(b) / n_calls
 
 
-def calls_for(ms_per_call, min_rep_ms=MIN_REP_MS):
-    return int(min(MAX_CALLS, max(MIN_CALLS, math.ceil(min_rep_ms / max(ms_per_call, 1e-6)))))
+def calls_for(ms_per_call, min_rep_ms=None):
+    """Calls per timed replay: at least MIN_CALLS and at least min_rep_ms of work."""
+    rep_ms = MIN_REP_MS if min_rep_ms is None else min_rep_ms
+    return int(min(MAX_CALLS, max(MIN_CALLS, math.ceil(rep_ms / max(ms_per_call, 1e-6)))))
 
 
 def graph_time(torch, fn, n_calls, warmup, reps=REPS, out=None):
@@ -624,7 +626,11 @@ def main():
     ap.add_argument("--only", default="", help="comma-separated secondary workload keys")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=8.0)
+    ap.add_argument("--min-rep-ms", type=float, default=50.0,
+                    help="minimum length of a timed replay of a secondary workload (profiling runs lower it)")
     args = ap.parse_args()
+    global MIN_REP_MS
+    MIN_REP_MS = args.min_rep_ms
 
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: the decode, prefill and "
