@@ -244,6 +244,29 @@ def bench_read_probe(torch, probe, reps):
             "frac_hbm_peak": round(shapes[best] / HBM_PEAK_GBPS, 4)}
 
 
+def probe_at_size(torch, probe, nbytes, reps, cache):
+    """The read probe over exactly ``nbytes`` per call (windows rotating over
+    2 GiB, so no call is served by the last-level cache), best of a few launch
+    shapes: the read rate a streaming kernel reaches at this transfer size,
+    fixed launch and latency costs included."""
+    key = int(nbytes)
+    if key in cache:
+        return cache[key]
+    if "buf" not in cache:
+        cache["buf"] = torch.ones(1 << 31, dtype=torch.uint8, device=DEV)
+    buf = cache["buf"]
+    # (transfers beyond the 2 GiB buffer: its whole size, where the rate no longer depends on size)
+    n = max(16, (min(int(nbytes), buf.numel()) // 16) * 16)
+    nwin = max(1, buf.numel() // n)
+    views = [buf[i * n:(i + 1) * n] for i in range(nwin)]
+    best = None
+    for blocks, unroll in ((512, 4), (1024, 4), (2048, 4), (2048, 8)):
+        t = graph_time(torch, lambda i: probe.read(views[i % nwin], blocks, unroll), 200, 5, reps=reps)
+        best = t["median_ms"] if best is None else min(best, t["median_ms"])
+    cache[key] = {"bytes": n, "us": round(best * 1e3, 2), "GBps": round(n / (best * 1e-3) / 1e9, 1)}
+    return cache[key]
+
+
 def bench_copy_probe(torch, reps):
     """Plain device-to-device copy of 1 GiB (read + write): the counter calibration kernel."""
     n = 1 << 29
@@ -615,6 +638,123 @@ HEADLINE_KEY = "llama7b_decode_G8"
 
 
 # ---------------------------------------------------------------------------
+# --timeline: per-workgroup phases of the matrix-core decode (libgqa_timeline.so)
+# ---------------------------------------------------------------------------
+
+TIMELINE_WORKLOADS = [("llama7b_decode_bf16", 8), ("llama7b_decode_bf16", 1), ("llama7b_decode_bf16", 4),
+                      ("llama7b_decode_bf16", 32), ("t5xxl_cross_decode_bf16", 8)]
+TICK_US = 0.01          # the device clock read by the timeline build runs at 100 MHz
+
+
+def _by_xcd(t, rows, col):
+    """Median of phase ``col`` over the workgroups of each XCD (slot 7 of the timeline)."""
+    import numpy as np
+    out = {}
+    for x in range(8):
+        vals = np.concatenate([r[t[c][t[c][:, 0] != 0][:, 7] == x, col] for c, r in enumerate(rows)])
+        vals = vals[~np.isnan(vals)]
+        if vals.size:
+            out[str(x)] = round(float(np.median(vals)), 2)
+    return out
+
+
+def timeline(torch, synth, n_calls=40):
+    """Phase timestamps of every workgroup over n_calls graph-replayed decode calls.
+
+    Per workgroup: 0 start, 1 length known, 2 first tile done, 3 tile loop done,
+    4 partial (or output) stored and acknowledged, 5 arrival counted, 6 end;
+    times are taken relative to the earliest start of the same call."""
+    import numpy as np
+    import grouped_query_decode_amd as gqa
+    path = os.path.join(os.path.dirname(gqa.library_path()), "libgqa_timeline.so")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.gqa_decode_split.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, sz, vp]
+    lib.gqa_decode_split.restype = i32
+    lib.gqa_timeline_set_buffer.argtypes = [vp]
+    lib.gqa_decode_num_splits.argtypes = [i32] * 5
+    lib.gqa_decode_workspace_bytes.argtypes = [i32] * 6
+    lib.gqa_decode_workspace_bytes.restype = sz
+    result = {}
+    for name, G in TIMELINE_WORKLOADS:
+        w = synth.WORKLOADS[name]
+        B, H, d, N = w.B, w.H, w.d, w.N
+        kv_bytes = 2 * B * G * N * d * 2
+        R = max(1, min(256, math.ceil((1 << 30) / kv_bytes)))
+        reps_in = [synth.decode_inputs(B, H, G, d, N, dtype="bf16", seed=w.seed + r, device=DEV) for r in range(R)]
+        out = torch.empty_like(reps_in[0]["q"])
+        ws = torch.zeros(max(int(lib.gqa_decode_workspace_bytes(B, H, G, d, N, 0)), 1), dtype=torch.uint8,
+                         device=DEV)
+        S = int(lib.gqa_decode_num_splits(B, H, G, d, N))
+        grid_max = B * G * S * 2
+        tl = torch.zeros((n_calls, grid_max, 8), dtype=torch.int64, device=DEV)
+        stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)   # noqa: E731
+
+        def call(i, buf):
+            x = reps_in[i % R]
+            lib.gqa_timeline_set_buffer(ctypes.c_void_p(buf))
+            st = lib.gqa_decode_split(ctypes.c_void_p(x["q"].data_ptr()), ctypes.c_void_p(x["k_cache"].data_ptr()),
+                                      ctypes.c_void_p(x["v_cache"].data_ptr()),
+                                      ctypes.c_void_p(x["seqlens"].data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                      B, H, G, d, N, synth.scale_for(d), 1, 0, ctypes.c_void_p(ws.data_ptr()),
+                                      ws.numel(), stream())
+            assert st == 0, st
+
+        for i in range(20):
+            call(i, None)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n_calls):
+                call(i, tl[i].data_ptr())
+        lib.gqa_timeline_set_buffer(None)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        tl.zero_()
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ev_us = a.elapsed_time(b) * 1e3 / n_calls
+        t = tl.cpu().numpy()
+        rows = []
+        for c in range(n_calls):
+            used = t[c][t[c][:, 0] != 0]
+            t0 = used[:, 0].min()
+            rel = (used[:, :7] - t0).astype(np.float64) * TICK_US
+            rel[used[:, :7] == 0] = np.nan
+            rows.append(rel)
+        def phase(col):
+            """Median over calls of the median and of the latest workgroup of phase col."""
+            meds, maxs = [], []
+            for r in rows:
+                v = r[:, col]
+                v = v[~np.isnan(v)]
+                if v.size:
+                    meds.append(float(np.median(v)))
+                    maxs.append(float(v.max()))
+            if not meds:
+                return None
+            return {"median": round(float(np.median(meds)), 2), "latest": round(float(np.median(maxs)), 2)}
+
+        merges = []
+        for r in rows:
+            last = r[~np.isnan(r[:, 5]) & ~np.isnan(r[:, 6])]
+            if len(last):
+                merges.append(float(np.median(last[:, 6] - last[:, 5])))
+        result[f"{name}:G{G}"] = {
+            "workgroups": int(np.sum(t[0][:, 0] != 0)), "splits": S, "event_us_per_call": round(ev_us, 2),
+            "started": phase(0), "length_known": phase(1), "first_tile_done": phase(2),
+            "loop_done": phase(3), "stored": phase(4), "counted": phase(5), "end": phase(6),
+            "merge_us_median": round(float(np.median(merges)), 2) if merges else None,
+            "loop_done_median_by_xcd": _by_xcd(t, rows, 3),
+        }
+        del reps_in, tl, g
+        torch.cuda.empty_cache()
+    return result
+
+
+# ---------------------------------------------------------------------------
 
 def main():
     ap = argparse.ArgumentParser()
@@ -626,6 +766,8 @@ def main():
     ap.add_argument("--only", default="", help="comma-separated secondary workload keys")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=8.0)
+    ap.add_argument("--timeline", action="store_true",
+                    help="print per-workgroup decode phase timings (libgqa_timeline.so) instead of the bench line")
     ap.add_argument("--min-rep-ms", type=float, default=50.0,
                     help="minimum length of a timed replay of a secondary workload (profiling runs lower it)")
     args = ap.parse_args()
@@ -644,6 +786,9 @@ def main():
     gqa.load_library()
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
+    if args.timeline:
+        print(json.dumps({"decode_timeline": timeline(torch, synth)}), flush=True)
+        return
     probe = ReadProbe(torch)
     flusher = ColdFlusher(torch, probe)
     means = stored_kernel_means()
@@ -725,9 +870,16 @@ def main():
         secondary["hbm_read_probe"] = bench_read_probe(torch, probe, reps)
         ceiling = secondary["hbm_read_probe"]["GBps"]
     if ceiling:
+        sized = {}
         for v in [head] + list(secondary.values()):
             if isinstance(v, dict) and "roofline" in v and v["roofline"]["bound"] == "hbm":
-                v["roofline"]["frac_of_measured_read_ceiling"] = round(v["GBps"] / ceiling, 4)
+                r = v["roofline"]
+                r["frac_of_measured_read_ceiling"] = round(v["GBps"] / ceiling, 4)
+                at = probe_at_size(torch, probe, v["bytes_per_call"], reps, sized)
+                r["read_probe_at_same_bytes"] = {"us": at["us"], "GBps": at["GBps"]}
+                r["frac_of_read_probe_at_same_bytes"] = round(v["GBps"] / at["GBps"], 4)
+        sized.pop("buf", None)
+        torch.cuda.empty_cache()
 
     roofline = dict(head["roofline"])
     roofline["traffic"] = stored_traffic()

@@ -3,9 +3,12 @@
     python -m grouped_query_decode_amd.build      # or build() from Python
 
 Every source in csrc/ is compiled to an object in _build/ (in parallel) and the
-objects are linked into grouped_query_decode_amd/libgqa.so; the benchmark's
-measurement probes (csrc/probe/) go into a separate libgqa_probe.so.  Packed
-float32 instructions are disabled for all device code.
+objects are linked into grouped_query_decode_amd/libgqa.so.  Two measurement
+libraries are built beside it: libgqa_probe.so (the benchmark's HBM read
+probe, csrc/probe/) and libgqa_timeline.so (the same sources compiled with
+GQA_DECODE_TIMELINE: the matrix-core decode kernel also records per-workgroup
+phase timestamps; used by ``bench.py --timeline`` only).  Packed float32
+instructions are disabled for all device code.
 """
 
 from __future__ import annotations
@@ -23,6 +26,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libgqa.so")
 PROBE_DIR = os.path.join(CSRC, "probe")
 PROBE_LIB_PATH = os.path.join(PKG_DIR, "libgqa_probe.so")
+TIMELINE_LIB_PATH = os.path.join(PKG_DIR, "libgqa_timeline.so")
 
 ARCH = "gfx950"
 COMMON_FLAGS = [
@@ -45,9 +49,11 @@ def sources(folder: str = CSRC) -> list[str]:
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
-def _compile(src: str, cc: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.relpath(src, CSRC).replace(os.sep, "__") + ".o")
+def _compile(src: str, cc: str, variant: str = "") -> str:
+    obj = os.path.join(BUILD_DIR, variant + os.path.relpath(src, CSRC).replace(os.sep, "__") + ".o")
     cmd = [cc, "-x", "hip", "-c", src, "-o", obj] + COMMON_FLAGS
+    if variant == "timeline__":
+        cmd.append("-DGQA_DECODE_TIMELINE=1")
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
@@ -68,13 +74,16 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
     probe_srcs = sources(PROBE_DIR)
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probe_srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, cc), srcs + probe_srcs))
-    _link(objs[:len(srcs)], cc, LIB_PATH)
-    _link(objs[len(srcs):], cc, PROBE_LIB_PATH)
+    jobs = [(s, "") for s in srcs + probe_srcs] + [(s, "timeline__") for s in srcs]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], cc, j[1]), jobs))
+    n, m = len(srcs), len(probe_srcs)
+    _link(objs[:n], cc, LIB_PATH)
+    _link(objs[n:n + m], cc, PROBE_LIB_PATH)
+    _link(objs[n + m:], cc, TIMELINE_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH} from {len(srcs)} sources and {PROBE_LIB_PATH} from "
-              f"{len(probe_srcs)}")
+        print(f"built {LIB_PATH} from {n} sources, {PROBE_LIB_PATH} from {m}, "
+              f"{TIMELINE_LIB_PATH} from {n}")
     return LIB_PATH
 
 

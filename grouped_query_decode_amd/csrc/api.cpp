@@ -19,6 +19,12 @@ namespace {
 
 thread_local std::string g_last_error;
 
+#ifdef GQA_DECODE_TIMELINE
+// Measurement build only (libgqa_timeline.so): where the matrix-core decode
+// kernel writes its per-workgroup phase timestamps.
+uint64_t* g_timeline = nullptr;
+#endif
+
 gqa_status fail(gqa_status s, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -201,6 +207,9 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
     p.scale = scale;
     p.num_splits = S;
     p.split_len = split_len;
+#ifdef GQA_DECODE_TIMELINE
+    p.timeline = g_timeline;
+#endif
     gqa_status st = launched(gqa::launch_decode_mfma(p, stream), "gqa_decode");
     if (st != GQA_OK || S == 1 || p.counters != nullptr) return st;
   } else {
@@ -480,6 +489,12 @@ const char* gqa_status_string(int status) {
 const char* gqa_last_error(void) { return g_last_error.c_str(); }
 
 int gqa_version(void) { return 100; }
+
+#ifdef GQA_DECODE_TIMELINE
+// Measurement build only: device buffer of 8 uint64 per workgroup of the next
+// matrix-core decode launches (NULL: none recorded).
+void gqa_timeline_set_buffer(uint64_t* buf) { g_timeline = buf; }
+#endif
 
 gqa_status gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* seqlens, void* out, int B, int H, int G, int d,

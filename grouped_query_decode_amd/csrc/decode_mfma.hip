@@ -162,6 +162,24 @@ __device__ __forceinline__ void merge_item(const DecodeProblem& p, const UnitPar
                H16::pack2(Ob[0] * inv, Ob[1] * inv), H16::pack2(Ob[2] * inv, Ob[3] * inv)});
 }
 
+// Phase timestamps of the measurement build (libgqa_timeline.so): thread 0
+// of each workgroup writes the 100 MHz device clock at the start, when the
+// sequence length is known, after its first tile, at the end of its tile loop,
+// once its partial is stored (or its output written), once its arrival is
+// counted, and at its end; slot 7 is the XCD it ran on.  Nothing is recorded
+// in the library build.
+#ifdef GQA_DECODE_TIMELINE
+#define GQA_PHASE(k)                                                                           \
+  do {                                                                                         \
+    if (threadIdx.x == 0 && p.timeline != nullptr)                                             \
+      p.timeline[(blockIdx.x + int64_t(blockIdx.y) * gridDim.x) * 8 + (k)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define GQA_PHASE(k) \
+  do {               \
+  } while (0)
+#endif
+
 template <int D, int NHB, int DT>
 __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(DecodeProblem p) {
   using C = Cfg<D>;
@@ -169,6 +187,12 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   __shared__ __attribute__((aligned(16))) char smem[C::kLds];
   __shared__ int s_last;
 
+  GQA_PHASE(0);
+#ifdef GQA_DECODE_TIMELINE
+  if (threadIdx.x == 0 && p.timeline != nullptr)
+    p.timeline[(blockIdx.x + int64_t(blockIdx.y) * gridDim.x) * 8 + 7] =
+        __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11));
+#endif
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int nw = blockDim.x >> 6;
@@ -180,14 +204,22 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   // by index, so every XCD gets an even share of each split index (with
   // ragged lengths the late splits are the ones that are often empty), and
   // the first splits, which are never empty, start first.
+  // Work group g (its n_rep queries; kv_div work groups share a K/V head when
+  // a group has more than 16 queries) of sequence b reads K/V head g_kv.  The
+  // grid is (splits x sequences x K/V heads, kv_div): the hardware deals
+  // workgroups to the 8 XCDs round-robin by linear index, so the kv_div work
+  // groups of one K/V head, a whole grid row apart, run on one XCD whenever
+  // the row length is a multiple of 8, and the second read of every K/V row
+  // is served by that XCD's L2 instead of HBM.
   const int S = p.num_splits;
-  const int units = p.B * p.G;
-  const int s = int(blockIdx.x / unsigned(units));
-  const int unit = int(blockIdx.x % unsigned(units));
-  const int g = unit % p.G;                // work group: its n_rep queries
-  const int b = unit / p.G;
-  const int g_kv = g / p.kv_div;           // the K/V head they read
   const int G_kv = p.G / p.kv_div;
+  const int units = p.B * G_kv;
+  const int s = int(blockIdx.x / unsigned(units));
+  const int r = int(blockIdx.x % unsigned(units));
+  const int b = r / G_kv;
+  const int g_kv = r - b * G_kv;
+  const int g = g_kv * p.kv_div + int(blockIdx.y);
+  const int unit = b * p.G + g;             // counters and partials of the work group
 
   const int raw_len = p.seqlens[b];
   const int len = raw_len < 0 ? 0 : (raw_len > p.n_max ? p.n_max : raw_len);
@@ -197,6 +229,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   // split leaves a (possibly empty) partial.
   const int ns = p.counters == nullptr ? S : max(1, min(S, (len + p.split_len - 1) / p.split_len));
   if (s >= ns) return;
+  GQA_PHASE(1);
   const int j0 = s * p.split_len;
   const int j1 = min(len, j0 + p.split_len);
 
@@ -371,8 +404,10 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   // position, so the running maximum is finite by then.)
   for (; tile < ntiles; tile += 2 * nw) {
     process(tile, ka, va, nvalid, true);
+    if (tile == wave) GQA_PHASE(2);
     process(tile + nw, kb2, vb2, nvalid, true);
   }
+  GQA_PHASE(3);
   if (owner) {
     // the appended token, as a one-row tile on wave 0 (its k, v from LDS)
     __syncthreads();
@@ -458,7 +493,15 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
       }
     }
   }
-  if (ns == 1 || p.counters == nullptr) return;
+  if (ns == 1 || p.counters == nullptr) {
+#ifdef GQA_DECODE_TIMELINE
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    GQA_PHASE(4);
+    GQA_PHASE(6);
+#endif
+    return;
+  }
 
   // Split merge by the last workgroup of this (b, g) to finish.  Each thread
   // waits until its device-coherent partial stores are acknowledged before the
@@ -466,30 +509,40 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   // every partial back with device-coherent loads issued after that.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  GQA_PHASE(4);
   if (threadIdx.x == 0) {
     const int old = atomicAdd(p.counters + unit, 1);
     s_last = (old == ns - 1);
   }
   __syncthreads();
-  if (!s_last) return;
+  GQA_PHASE(5);
+  if (!s_last) {
+    GQA_PHASE(6);
+    return;
+  }
   if (threadIdx.x == 0)            // ready for the next call (nothing reads it in this one)
     __hip_atomic_store(p.counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   constexpr int kC8 = D / 8;
 #pragma unroll 1
   for (int t = threadIdx.x; t < p.n_rep * kC8; t += blockDim.x)
     merge_item<D, DT>(p, up, b, ns, g, t / kC8, t % kC8);
+#ifdef GQA_DECODE_TIMELINE
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  GQA_PHASE(6);
+#endif
 }
 
 template <int D, int NHB, int DT>
 hipError_t launch_t(const DecodeProblem& p, hipStream_t stream) {
-  const int64_t blocks = int64_t(p.B) * p.G * p.num_splits;
+  const int64_t blocks = int64_t(p.B) * (p.G / p.kv_div) * p.num_splits;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // one wave per 32-position tile of a split, at most four
   const int tiles = (p.split_len + kKT - 1) / kKT;
   const int waves = tiles >= 4 ? 4 : (tiles >= 2 ? 2 : 1);
-  hipLaunchKernelGGL((decode_mfma_kernel<D, NHB, DT>), dim3(unsigned(blocks)), dim3(64 * waves), 0,
-                     stream, p);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, NHB, DT>), dim3(unsigned(blocks), unsigned(p.kv_div)),
+                     dim3(64 * waves), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -514,6 +567,8 @@ hipError_t launch_dt(const DecodeProblem& p, hipStream_t stream) {
 
 hipError_t launch_decode_mfma(const DecodeProblem& p, hipStream_t stream) {
   if (!abi_ok(p)) return kAbiMismatch;
+  if (p.B <= 0 || p.num_splits <= 0) return hipSuccess;
+  if (p.kv_div < 1 || p.G < 1 || p.G % p.kv_div != 0) return hipErrorInvalidValue;
   return p.dtype == kF16 ? launch_dt<kF16>(p, stream) : launch_dt<kBF16>(p, stream);
 }
 

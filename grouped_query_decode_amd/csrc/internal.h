@@ -94,6 +94,9 @@ struct DecodeProblem {
   int kv_div;
   float scale;
   int num_splits, split_len;
+#ifdef GQA_DECODE_TIMELINE
+  uint64_t* timeline;       // [grid][8] phase timestamps (the timeline build only)
+#endif
 };
 
 struct CombineProblem {
