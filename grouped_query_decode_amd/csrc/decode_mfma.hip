@@ -355,8 +355,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
           t2[blk][r] = x;
           tmax = fmaxf(tmax, x);
         }
-      tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+      tmax = max_over_rows(tmax);
       const float mn = fmaxf(mrun[hb], tmax);      // finite: the tile's first position is valid
       const float alpha = __builtin_amdgcn_exp2f(mrun[hb] - mn);
       mrun[hb] = mn;

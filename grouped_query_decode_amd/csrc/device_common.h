@@ -103,6 +103,43 @@ __device__ __forceinline__ float reduce_sum_lanes(float v) {
   return v;
 }
 
+// Sum over aligned groups of WIDTH lanes (1 .. 64), every lane of a group
+// receiving the group's sum, without the LDS crossbar: DPP quad permutations
+// (lane ^ 1, lane ^ 2), the half-row and row mirrors (after the quad steps
+// every lane of a quad holds the quad's sum, so the mirror partner holds the
+// other quad's or half-row's), then gfx950's row-swap instructions for 32 and
+// 64 lanes.  Float addition is commutative, so every lane of a group ends with
+// the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int WIDTH>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  if constexpr (WIDTH >= 2) v += dpp_mov<0xB1>(v);     // quad_perm [1,0,3,2]
+  if constexpr (WIDTH >= 4) v += dpp_mov<0x4E>(v);     // quad_perm [2,3,0,1]
+  if constexpr (WIDTH >= 8) v += dpp_mov<0x141>(v);    // row_half_mirror
+  if constexpr (WIDTH >= 16) v += dpp_mov<0x140>(v);   // row_mirror
+  if constexpr (WIDTH >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (WIDTH >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return v;
+}
+
+// Maximum over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48),
+// every lane receiving it, with gfx950's row-swap instructions.
+__device__ __forceinline__ float max_over_rows(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+
 // Compiler barrier plus a wait for this wave's outstanding LDS operations.
 __device__ __forceinline__ void lds_wave_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

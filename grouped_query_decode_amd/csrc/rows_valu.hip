@@ -6,12 +6,16 @@
 //   out = sum_j softmax_j(scale * q . K[j]) V[j]   over the attended positions.
 //
 // Work unit: one workgroup (4 waves) per (row, K/V head, split, block of up to
-// 8 heads of the group).  Each cached position is read once per unit and used
-// by all heads of the block.  A position's d elements are spread over
-// d*sizeof/16 lanes (one 16-byte load each); several positions are in flight
-// per wave instruction.  Softmax is online, in base 2, in float32.  The four
-// waves take interleaved positions and merge their (max, sum, output) at the
-// end through LDS.
+// 8 heads of the group; the block size is a template parameter, the smallest
+// of 1, 2, 4, 8 that holds the group).  Each cached position is read once per
+// unit and used by all heads of the block.  A position's d elements are spread
+// over a lane group of d*sizeof/16 lanes (one 16-byte load each); several
+// lane groups, each with positions of its own, share a wave instruction.
+// Softmax is online, in base 2, in float32, and every lane group keeps its own
+// running (max, sum, output): inside the loop the only cross-lane step is the
+// dot product's sum over the lane group, and the heads' chains are independent
+// (no early exit), so their latencies overlap.  The lane groups, then the four
+// waves, merge their (max, sum, output) at the end.
 
 #include "device_common.h"
 #include "internal.h"
@@ -19,7 +23,7 @@
 namespace gqa {
 namespace {
 
-constexpr int kHeadsPerBlock = 8;
+constexpr int kMaxHeadsPerBlock = 8;
 constexpr int kWaves = 4;
 
 template <int DT>
@@ -66,7 +70,7 @@ struct Elem<kF16> {
   }
 };
 
-template <int DT, int D>
+template <int DT, int D, int kHeadsPerBlock>
 __global__ __launch_bounds__(256) void rows_valu_kernel(RowsProblem p) {
   using E = Elem<DT>;
   constexpr int EPL = 16 / E::kSize;   // elements per lane
@@ -77,6 +81,7 @@ __global__ __launch_bounds__(256) void rows_valu_kernel(RowsProblem p) {
   __shared__ float sm_m[kWaves][kHeadsPerBlock];
   __shared__ float sm_l[kWaves][kHeadsPerBlock];
   __shared__ float sm_o[kWaves][kHeadsPerBlock][D];
+  static_assert(kHeadsPerBlock >= 1 && kHeadsPerBlock <= kMaxHeadsPerBlock, "head block");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -137,52 +142,66 @@ __global__ __launch_bounds__(256) void rows_valu_kernel(RowsProblem p) {
   const char* kbase = static_cast<const char*>(p.k) + kv_off * E::kSize;
   const char* vbase = static_cast<const char*>(p.v) + kv_off * E::kSize;
 
-  for (int jb = j0 + wave * RPW; jb < j1; jb += kWaves * RPW) {
-    const int j = jb + r;
-    const bool valid = j < j1;
-    float kf[EPL], vf[EPL];
-    if (valid) {
-      const int64_t off = (int64_t(j) * p.kv_pos_stride + c * EPL) * E::kSize;
-      E::load16(kbase + off, kf);
-      E::load16(vbase + off, vf);
-    } else {
+  // Positions in batches of kUnroll wave steps: all their loads are issued
+  // before any of them is used, so the load latency is paid once per batch.
+  constexpr int kUnroll = 4;
+  for (int jb = j0 + wave * RPW; jb < j1; jb += kWaves * RPW * kUnroll) {
+    float kf[kUnroll][EPL], vf[kUnroll][EPL];
+    bool valid[kUnroll];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) kf[e] = vf[e] = 0.f;
+    for (int u = 0; u < kUnroll; ++u) {
+      const int j = jb + u * kWaves * RPW + r;
+      valid[u] = j < j1;
+      if (valid[u]) {
+        const int64_t off = (int64_t(j) * p.kv_pos_stride + c * EPL) * E::kSize;
+        E::load16(kbase + off, kf[u]);
+        E::load16(vbase + off, vf[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) kf[u][e] = vf[u][e] = 0.f;
+      }
     }
 #pragma unroll
-    for (int hh = 0; hh < kHeadsPerBlock; ++hh) {
-      if (hh >= nh) break;
-      float sc = 0.f;
+    for (int u = 0; u < kUnroll; ++u) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sc = fmaf(qf[hh][e], kf[e], sc);
-      sc = reduce_sum_lanes<LPR>(sc);
-      sc = valid ? sc : -INFINITY;
-      float mt = sc;
+      for (int hh = 0; hh < kHeadsPerBlock; ++hh) {
+        float sc = 0.f;
 #pragma unroll
-      for (int msk = LPR; msk < 64; msk <<= 1) mt = fmaxf(mt, shfl_xor(mt, msk));
-      const float mn = fmaxf(m[hh], mt);          // finite: position jb is valid
-      const float alpha = exp2f(m[hh] - mn);      // 0 on the first step
-      const float pj = valid ? exp2f(sc - mn) : 0.f;
-      float ps = pj;
+        for (int e = 0; e < EPL; ++e) sc = fmaf(qf[hh][e], kf[u][e], sc);
+        sc = lane_group_sum<LPR>(sc);
+        sc = valid[u] ? sc : -INFINITY;
+        // this lane group's running maximum (-inf until its first valid position)
+        const float mn = fmaxf(m[hh], sc);
+        const float alpha = mn == -INFINITY ? 1.f : exp2f(m[hh] - mn);
+        const float pj = valid[u] ? exp2f(sc - mn) : 0.f;
+        l[hh] = fmaf(l[hh], alpha, pj);
 #pragma unroll
-      for (int msk = LPR; msk < 64; msk <<= 1) ps += shfl_xor(ps, msk);
-      l[hh] = l[hh] * alpha + ps;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[hh][e] = fmaf(pj, vf[e], o[hh][e] * alpha);
-      m[hh] = mn;
+        for (int e = 0; e < EPL; ++e) o[hh][e] = fmaf(pj, vf[u][e], o[hh][e] * alpha);
+        m[hh] = mn;
+      }
     }
   }
 
-  // Sum the per-position partial outputs over the positions of this wave step.
+  // Merge the lane groups of the wave: rescale each to the wave's maximum,
+  // then sum (max, sum, output) over the groups.
 #pragma unroll
   for (int hh = 0; hh < kHeadsPerBlock; ++hh) {
+    float mw = m[hh];
+#pragma unroll
+    for (int msk = LPR; msk < 64; msk <<= 1) mw = fmaxf(mw, shfl_xor(mw, msk));
+    const float f = mw == -INFINITY ? 0.f : exp2f(m[hh] - mw);
+    float lw = l[hh] * f;
+#pragma unroll
+    for (int msk = LPR; msk < 64; msk <<= 1) lw += shfl_xor(lw, msk);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      float x = o[hh][e];
+      float x = o[hh][e] * f;
 #pragma unroll
       for (int msk = LPR; msk < 64; msk <<= 1) x += shfl_xor(x, msk);
       o[hh][e] = x;
     }
+    m[hh] = mw;
+    l[hh] = lw;
   }
   if (lane < LPR) {
 #pragma unroll
@@ -231,14 +250,32 @@ __global__ __launch_bounds__(256) void rows_valu_kernel(RowsProblem p) {
   }
 }
 
-template <int DT, int D>
-hipError_t launch_t(const RowsProblem& p, hipStream_t stream) {
-  const int n_hb = (p.n_rep + kHeadsPerBlock - 1) / kHeadsPerBlock;
+template <int DT, int D, int HB>
+hipError_t launch_hb(const RowsProblem& p, hipStream_t stream) {
+  const int n_hb = (p.n_rep + HB - 1) / HB;
   const int64_t blocks = int64_t(p.n_rows) * p.G * p.num_splits * n_hb;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((rows_valu_kernel<DT, D>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((rows_valu_kernel<DT, D, HB>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+// The smallest head block that holds the group (no padded heads below 8) --
+// halved while that leaves fewer workgroups than compute units: a small
+// problem then runs one or two heads per workgroup, many workgroups reading
+// the same rows (the repeats come from the caches), so that each workgroup's
+// dependent chain of softmax steps is short.
+template <int DT, int D>
+hipError_t launch_t(const RowsProblem& p, hipStream_t stream) {
+  int hb = p.n_rep <= 1 ? 1 : (p.n_rep <= 2 ? 2 : (p.n_rep <= 4 ? 4 : 8));
+  const int64_t units = int64_t(p.n_rows) * p.G * p.num_splits;
+  while (hb > 1 && units * ((p.n_rep + hb - 1) / hb) < 256) hb /= 2;
+  switch (hb) {
+    case 1: return launch_hb<DT, D, 1>(p, stream);
+    case 2: return launch_hb<DT, D, 2>(p, stream);
+    case 4: return launch_hb<DT, D, 4>(p, stream);
+    default: return launch_hb<DT, D, 8>(p, stream);
+  }
 }
 
 }  // namespace
