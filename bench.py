@@ -62,7 +62,7 @@ PREFILL_WARMUP = 120              # untimed prefill calls before timing (clock r
 HEADLINE = ("llama7b_decode_bf16", 8)
 METRIC = "decode KV-read GB/s (% of HBM peak) + tokens/s; prefill TFLOP/s (% MFMA)"
 KERNEL_SOURCE_DIR = os.path.join("grouped_query_decode_amd", "csrc")
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_llama7b_G8_hbm_counters.md")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 TRACE_FILE = os.path.join(ROOT, "profiles", "bench_kernel_trace.md")
 DEV = "cuda:0"
 
@@ -112,9 +112,10 @@ def _stored_json(path):
 
 
 def stored_traffic():
-    """HBM bytes per launch of the headline decode from the committed counter summary."""
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) per workload, from the committed
+    counter summary, while it still matches the library sources."""
     data = _stored_json(COUNTERS_FILE)
-    return None if data is None else data.get("traffic_bytes_per_launch")
+    return {} if data is None else data.get("traffic_bytes_per_launch", {})
 
 
 def stored_kernel_means():
@@ -221,6 +222,32 @@ class ReadProbe:
         self.torch = torch
         self.sink = torch.zeros(4, dtype=torch.int32, device=DEV)
 
+    def valu_rates(self, blocks=1024):
+        """SIMD cycles per wave64 instruction (fma, exp, and a 1:1 mix), at the measured clock."""
+        torch = self.torch
+        lib = self.lib
+        lib.gqa_probe_valu_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        lib.gqa_probe_valu_rate.restype = ctypes.c_int
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=DEV)
+        stream = torch.cuda.current_stream()
+        res = {}
+        for kind, name, per_step in ((0, "fma", 8), (1, "exp", 8), (2, "exp_plus_fma", 16)):
+            call = lambda: lib.gqa_probe_valu_rate(ctypes.c_void_p(out.data_ptr()), kind, blocks,  # noqa: E731
+                                                   ctypes.c_void_p(stream.cuda_stream))
+            call()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(5):
+                call()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / 5
+            # wave-instructions per SIMD: blocks x 4 waves / 1024 SIMDs x 4096 steps x per_step
+            wi = blocks * 4 / 1024 * 4096 * per_step
+            res[name] = {"ns_per_wave_instruction_per_simd": round(ms * 1e6 / wi, 4)}
+        return res
+
     def read(self, buf, blocks, unroll):
         rc = self.lib.gqa_probe_hbm_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
                                          ctypes.c_void_p(self.sink.data_ptr()), blocks, unroll,
@@ -282,11 +309,14 @@ def bench_copy_probe(torch, reps):
             "timing": "eager back-to-back calls (0.4 ms each: host dispatch is hidden)"}
 
 
+TRAFFIC = {}
+
+
 def _roofline_hbm(gbps, kernel, nbytes, key, means):
     mean = means.get(key)
     r = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
          "frac": round(gbps / HBM_PEAK_GBPS, 4), "kernel": kernel, "algorithmic_bytes_per_launch": nbytes,
-         "rocprof_kernel_mean_us": mean}
+         "rocprof_kernel_mean_us": mean, "traffic": TRAFFIC.get(key)}
     if mean:
         r["achieved_by_rocprof_mean"] = round(nbytes / (mean * 1e-6) / 1e9, 1)
         r["frac_by_rocprof_mean"] = round(r["achieved_by_rocprof_mean"] / HBM_PEAK_GBPS, 4)
@@ -390,7 +420,8 @@ def bench_prefill(torch, gqa, synth, n_calls, warmup, reps, flusher, means, key,
         "tokens_per_s": round(w.B * w.N / (t["median_ms"] * 1e-3), 1), "cold_latency_us": cold,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / BF16_PEAK_TFLOPS, 4), "kernel": "prefill_mfma_kernel",
-                     "algorithmic_flops_per_launch": fl, "rocprof_kernel_mean_us": mean},
+                     "algorithmic_flops_per_launch": fl, "rocprof_kernel_mean_us": mean,
+                     "traffic": TRAFFIC.get(key)},
     })
     if mean:
         res["roofline"]["achieved_by_rocprof_mean"] = round(fl / (mean * 1e-6) / 1e12, 1)
@@ -429,7 +460,7 @@ def bench_prefill_chunk(torch, gqa, synth, warmup, reps, means, key, ctx=2048, T
     res.update({"flops_per_call": fl, "TFLOPs": tf, "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
                 "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(tf / BF16_PEAK_TFLOPS, 4), "kernel": "prefill_mfma_kernel",
-                             "rocprof_kernel_mean_us": means.get(key)}})
+                             "rocprof_kernel_mean_us": means.get(key), "traffic": TRAFFIC.get(key)}})
     del x, q, out
     torch.cuda.empty_cache()
     return res
@@ -766,6 +797,8 @@ def main():
     ap.add_argument("--only", default="", help="comma-separated secondary workload keys")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=8.0)
+    ap.add_argument("--probe-rates", action="store_true",
+                    help="print the vector-unit issue rates (fma, exp) and exit")
     ap.add_argument("--timeline", action="store_true",
                     help="print per-workgroup decode phase timings (libgqa_timeline.so) instead of the bench line")
     ap.add_argument("--min-rep-ms", type=float, default=50.0,
@@ -790,8 +823,12 @@ def main():
         print(json.dumps({"decode_timeline": timeline(torch, synth)}), flush=True)
         return
     probe = ReadProbe(torch)
+    if args.probe_rates:
+        print(json.dumps({"valu_issue_rates": probe.valu_rates()}), flush=True)
+        return
     flusher = ColdFlusher(torch, probe)
     means = stored_kernel_means()
+    TRAFFIC.update(stored_traffic())
     want_cpu = not args.no_cpu_baseline
     only = set(filter(None, args.only.split(",")))
     run = (lambda k: (not args.quick) and (not only or k in only))   # noqa: E731
@@ -881,8 +918,9 @@ def main():
         sized.pop("buf", None)
         torch.cuda.empty_cache()
 
+    if not args.quick and not only:
+        secondary["valu_issue_rates"] = probe.valu_rates()
     roofline = dict(head["roofline"])
-    roofline["traffic"] = stored_traffic()
     roofline["kernel"] = "decode_mfma_kernel<128,1> (split merge fused)"
     line = {
         "metric": METRIC,

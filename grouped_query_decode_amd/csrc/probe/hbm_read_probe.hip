@@ -62,3 +62,49 @@ extern "C" int gqa_probe_hbm_read(const void* buf, size_t bytes, uint32_t* sink,
   }
   return e == hipSuccess ? 0 : 4;
 }
+
+// ---------------------------------------------------------------------------
+// Vector-unit issue rates: every lane runs 8 independent chains of N steps of
+// one instruction kind (kind 0: v_fma_f32; 1: v_exp_f32; 2: one of each per
+// step), so the time of a launch over the whole chip gives the SIMD cycles per
+// wave64 instruction of that kind (and whether an exp overlaps an FMA).
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kRateSteps = 4096;
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void valu_rate_kernel(float* out, float seed) {
+  float x[8], y[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    x[j] = seed * float(threadIdx.x + j);
+    y[j] = seed * float(j);
+  }
+  for (int i = 0; i < kRateSteps; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (KIND != 0) x[j] = __builtin_amdgcn_exp2f(-fabsf(x[j]));
+      if constexpr (KIND != 1) y[j] = fmaf(y[j], 0.999f, 0.0001f);
+    }
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r += x[j] + y[j];
+  out[int64_t(blockIdx.x) * kThreads + threadIdx.x] = r;
+}
+
+}  // namespace
+
+extern "C" int gqa_probe_valu_rate(float* out, int kind, int blocks, void* stream) {
+  if (!out || (reinterpret_cast<uintptr_t>(out) & 3u) || blocks < 1 || blocks > (1 << 16) || kind < 0 || kind > 2)
+    return 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kind == 0)
+    hipLaunchKernelGGL(valu_rate_kernel<0>, dim3(unsigned(blocks)), dim3(kThreads), 0, s, out, 0.001f);
+  else if (kind == 1)
+    hipLaunchKernelGGL(valu_rate_kernel<1>, dim3(unsigned(blocks)), dim3(kThreads), 0, s, out, 0.001f);
+  else
+    hipLaunchKernelGGL(valu_rate_kernel<2>, dim3(unsigned(blocks)), dim3(kThreads), 0, s, out, 0.001f);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}

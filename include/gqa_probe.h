@@ -30,6 +30,18 @@ extern "C" {
 int gqa_probe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, int unroll,
                        void* stream);
 
+/*
+ * gqa_probe_valu_rate - vector-unit issue rate: `blocks` workgroups of 256
+ * threads, every lane running 8 independent chains of 4096 steps of one
+ * instruction kind -- kind 0: v_fma_f32, 1: v_exp_f32 (on -|x|, so values stay
+ * in (0, 1]), 2: one of each per step.  The launch time over the whole chip
+ * gives the SIMD cycles per wave64 instruction of that kind, and kind 2 shows
+ * whether an exp overlaps an FMA.  out: device, blocks * 256 floats (written).
+ * Returns 0, 1 for an invalid argument (nothing enqueued), 4 if the launch was
+ * refused.
+ */
+int gqa_probe_valu_rate(float* out, int kind, int blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -55,7 +55,7 @@ def test_probe_library_exports_its_header():
         pytest.fail("libgqa_probe.so is not built: run __graft_entry__.build() first")
     raw = ctypes.CDLL(path)
     names = declared_functions(os.path.join(ROOT, "include", "gqa_probe.h"))
-    assert names == ["gqa_probe_hbm_read"]
+    assert names == ["gqa_probe_hbm_read", "gqa_probe_valu_rate"]
     for name in names:
         assert hasattr(raw, name)
     f = raw.gqa_probe_hbm_read
@@ -68,6 +68,12 @@ def test_probe_library_exports_its_header():
     assert f(P_MIS, 1 << 20, P, 1024, 8, None) == 1       # misaligned
     assert f(ctypes.c_void_p(0), 1 << 20, P, 1024, 8, None) == 1
     assert f(P, 1 << 20, P, 0, 8, None) == 1              # blocks
+    r = raw.gqa_probe_valu_rate
+    r.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    r.restype = ctypes.c_int
+    assert r(P, 3, 1024, None) == 1                       # kind
+    assert r(ctypes.c_void_p(0), 0, 1024, None) == 1
+    assert r(P, 0, 0, None) == 1
 
 
 def test_status_strings(lib):
