@@ -24,8 +24,12 @@
 //           after the scores
 //
 // Each wave walks its own 32-position tiles of the split (tile t goes to wave
-// t mod waves) with two tiles in flight in alternating register sets; the
-// waves merge (max, sum, output) through LDS.  With several splits, each
+// t mod waves) with one tile in flight: the next tile's loads go out as soon
+// as the score MFMAs have read this tile's K registers and its V rows are in
+// LDS, and land during the softmax and the weighted sum (two tiles in flight
+// per wave measured ~5% slower: the extra requests in the memory system cost
+// more than the latency they hide).  The waves merge (max, sum, output)
+// through LDS.  With several splits, each
 // workgroup writes its partial (max, sum, output) per head; the last workgroup
 // of a (b, g) to finish -- found with a counter in the workspace header, which
 // it resets -- merges the partials (log-sum-exp) and writes the output, so one
@@ -337,8 +341,8 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
           a = mfma16<DT>(kr[blk][ks], qop[hb][ks], a);
         sacc[hb][blk] = a;
       }
-    // this tile's registers are free: fetch the tile after next into them
-    if (prefetch) load_tile(tile + 2 * nw, kr, vr);
+    // this tile's registers are free: fetch the wave's next tile into them
+    if (prefetch) load_tile(tile + nw, kr, vr);
 
     // online softmax; lane holds keys 16*blk + 4*hi + r of the tile, head lo
     const int rel0 = tile * kKT + 4 * hi;
@@ -389,22 +393,16 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
     }
   };
 
-  // Wave w takes tiles w, w + nw, w + 2 nw, ... with two tiles in flight: the
-  // two register sets alternate, so no register copies (and no full wait on
-  // outstanding loads) sit between a tile's loads and its use.
+  // Wave w takes tiles w, w + nw, w + 2 nw, ...; each tile's processing
+  // issues the loads of the next one into the registers it has just freed.
   const int ntiles = (nvalid + kKT - 1) / kKT;
-  KTile ka, kb2;
-  VTile va, vb2;
+  KTile ka;
+  VTile va;
   int tile = wave;
   load_tile(tile, ka, va);
-  load_tile(tile + nw, kb2, vb2);
-  // (A wave's second tile may lie past the end: all its scores are masked, so
-  // it changes nothing -- the first tile of the pair always has a valid
-  // position, so the running maximum is finite by then.)
-  for (; tile < ntiles; tile += 2 * nw) {
+  for (; tile < ntiles; tile += nw) {
     process(tile, ka, va, nvalid, true);
     if (tile == wave) GQA_PHASE(2);
-    process(tile + nw, kb2, vb2, nvalid, true);
   }
   GQA_PHASE(3);
   if (owner) {
@@ -549,7 +547,7 @@ hipError_t launch_t(const DecodeProblem& p, hipStream_t stream) {
 
 bool decode_mfma_supports(int n_rep, int d, int num_splits, int split_len) {
   // Byte offsets of the buffer instructions are 32-bit: a split's K/V bytes
-  // (plus the prefetch of up to 2 x 4 tiles past its end) and a unit's
+  // (plus the prefetch of up to 4 tiles past its end, with margin) and a unit's
   // partial results must stay below 2^31.
   const int64_t reach = (int64_t(split_len) + 16 * kKT) * d * 2;
   const int64_t partials = int64_t(n_rep) * num_splits * d * 4;
