@@ -50,11 +50,11 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // that every CU streams its share of the cache at once; more splits than
 // that cost more in the merge of the partial results (written, counted and
 // read back once per split) than they gain.  Splits are whole 32-position
-// tiles and at least 256 positions long, which bounds the merge work per
+// tiles and at least 128 positions long, which bounds the merge work per
 // position; long caches are cut into slices of at most 2048 positions so that
 // ragged lengths balance across the machine.
 constexpr int64_t kTargetWorkgroups = 256;
-constexpr int64_t kMinSplitLen = 256;
+constexpr int64_t kMinSplitLen = 128;
 constexpr int64_t kMaxSplitLen = 2048;
 
 bool decode_shape_valid(int B, int H, int G, int d, int n_max) {
