@@ -768,16 +768,19 @@ def timeline(torch, synth, n_calls=40):
                 return None
             return {"median": round(float(np.median(meds)), 2), "latest": round(float(np.median(maxs)), 2)}
 
+        # the merging workgroup of a (b, g) is the one whose end comes long
+        # after its count (the others end right after counting in): per call,
+        # the longest count-to-end span is the slowest merge
         merges = []
         for r in rows:
-            last = r[~np.isnan(r[:, 5]) & ~np.isnan(r[:, 6])]
-            if len(last):
-                merges.append(float(np.median(last[:, 6] - last[:, 5])))
+            both = r[~np.isnan(r[:, 5]) & ~np.isnan(r[:, 6])]
+            if len(both):
+                merges.append(float(np.max(both[:, 6] - both[:, 5])))
         result[f"{name}:G{G}"] = {
             "workgroups": int(np.sum(t[0][:, 0] != 0)), "splits": S, "event_us_per_call": round(ev_us, 2),
             "started": phase(0), "length_known": phase(1), "first_tile_done": phase(2),
             "loop_done": phase(3), "stored": phase(4), "counted": phase(5), "end": phase(6),
-            "merge_us_median": round(float(np.median(merges)), 2) if merges else None,
+            "slowest_merge_us": round(float(np.median(merges)), 2) if merges else None,
             "loop_done_median_by_xcd": _by_xcd(t, rows, 3),
         }
         del reps_in, tl, g
