@@ -13,7 +13,8 @@
 // head, the repeat coming mostly from the last-level cache):
 //
 //   scores  S^T[key][head] = K[key][:] . Q[head][:]     16x16x32 16-bit MFMA,
-//           A = 16 keys x 32 dims straight from HBM (16-byte loads),
+//           A = 16 keys x 32 dims read from the wave's LDS copy of the K
+//           tile (loaded as whole contiguous rows, 1 KB per instruction),
 //           B = the group's queries (registers, loaded once)
 //   softmax online, base 2 (hardware exp2), float32; the weights are rounded
 //           to the 16-bit format and the normaliser sums the rounded weights
@@ -25,10 +26,11 @@
 //
 // Each wave walks its own 32-position tiles of the split (tile t goes to wave
 // t mod waves) with one tile in flight: the next tile's loads go out as soon
-// as the score MFMAs have read this tile's K registers and its V rows are in
-// LDS, and land during the softmax and the weighted sum (two tiles in flight
-// per wave measured ~5% slower: the extra requests in the memory system cost
-// more than the latency they hide).  The waves merge (max, sum, output)
+// as this tile's K and V rows are in LDS, and land during its scores, softmax
+// and weighted sum (two tiles in flight per wave measured ~5% slower: the
+// extra requests in the memory system cost more than the latency they hide;
+// K loaded straight into the MFMA's register layout -- 64 bytes of each of
+// 16 rows per instruction instead of 1 KB of contiguous rows -- 2-6% slower).  The waves merge (max, sum, output)
 // through LDS.  With several splits, each
 // workgroup writes its partial (max, sum, output) per head; the last workgroup
 // of a (b, g) to finish -- found with a counter in the workspace header, which
@@ -54,11 +56,16 @@ struct Cfg {
   static constexpr int kChunks = D / 8;           // 16-byte chunks per cached row
   static constexpr int kVLoads = kKT * kChunks / 64;
   static constexpr int kPitch = D * 2 + 32;       // LDS bytes per V row (transposing reads hit distinct banks)
-  static constexpr int kWaveLds = kKT * kPitch;
+  static constexpr int kKBytes = kKT * D * 2;     // LDS bytes per K tile (rows unpadded, chunks permuted)
+  static constexpr int kWaveLds = kKT * kPitch + kKBytes;
   static constexpr int kMergeRow = D + 4;         // floats per head row in the merge area
   static constexpr int kMergeBytes = (kMaxWaves * 16 * kMergeRow + 2 * kMaxWaves * 16) * 4;
   static constexpr int kLds = kMaxWaves * kWaveLds > kMergeBytes ? kMaxWaves * kWaveLds : kMergeBytes;
 };
+
+// K tile rows in LDS: 16-byte chunk c of row r at position c ^ kswz(r)
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
@@ -285,6 +292,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   }
   const float c2 = p.scale * kLog2e;
   char* myv = smem + wave * C::kWaveLds;
+  char* myk = myv + kKT * C::kPitch;
 
   // Positions [j0, j1) through buffer resources that end at j1: loads past
   // the end return zeros without touching memory, so the loads need no
@@ -293,20 +301,17 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   const uint32_t vbytes = uint32_t(nvalid) * uint32_t(D * 2);
   const __amdgpu_buffer_rsrc_t rk = rsrc(kb + int64_t(j0) * D, vbytes);
   const __amdgpu_buffer_rsrc_t rv = rsrc(vb + int64_t(j0) * D, vbytes);
-  // K straight into the score MFMA's A layout: lane (lo, hi) of key block blk,
-  // k-step ks holds row 16*blk + lo, 16-byte chunk 4*ks + hi.  V rows land
-  // 16 bytes per lane, 64 lanes per load covering 64 / kChunks whole rows.
-  const int k_lane = (lo * D + hi * 8) * 2;
+  // K and V rows land 16 bytes per lane, each 64-lane load covering 64 /
+  // kChunks whole rows (1 KB of contiguous cache), and go through the wave's
+  // LDS area: K in the score MFMA's A layout, V for the transposing reads.
   const int v_lane = lane * 16;
-  typedef u32x4_t KTile[2][C::kSteps];
+  typedef u32x4_t KTile[C::kVLoads];
   typedef u32x4_t VTile[C::kVLoads];
   auto load_tile = [&](int tile, KTile& kr, VTile& vr) {
     const int base = tile * (kKT * D * 2);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int ks = 0; ks < C::kSteps; ++ks)
-        kr[blk][ks] = __builtin_amdgcn_raw_buffer_load_b128(rk, base + k_lane + blk * (16 * D * 2) + ks * 64, 0, 0);
+    for (int t = 0; t < C::kVLoads; ++t)
+      kr[t] = __builtin_amdgcn_raw_buffer_load_b128(rk, base + v_lane + t * 1024, 0, 0);
 #pragma unroll
     for (int t = 0; t < C::kVLoads; ++t)
       vr[t] = __builtin_amdgcn_raw_buffer_load_b128(rv, base + v_lane + t * 1024, 0, kNonTemporal);
@@ -323,13 +328,27 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   const int vt_lane = (4 * hi + (lo >> 2)) * C::kPitch + (lo & 3) * 8;
 
   auto process = [&](int tile, KTile& kr, VTile& vr, int nv, bool prefetch) {
-    // V rows of this tile into the wave's LDS area (padded rows)
+    // K rows of this tile into the wave's LDS area, chunk c of row r at
+    // position c ^ kswz(r) (unpadded rows; the A-operand reads below then hit
+    // every bank once per 16 lanes), and V rows (padded rows)
 #pragma unroll
     for (int t = 0; t < C::kVLoads; ++t) {
       const int idx = t * 64 + lane;
-      *reinterpret_cast<u32x4_t*>(myv + (idx / C::kChunks) * C::kPitch + (idx % C::kChunks) * 16) = vr[t];
+      const int r = idx / C::kChunks, c = idx % C::kChunks;
+      *reinterpret_cast<u32x4_t*>(myk + r * (D * 2) + ((c ^ kswz<D>(r)) << 4)) = kr[t];
+      *reinterpret_cast<u32x4_t*>(myv + r * C::kPitch + c * 16) = vr[t];
     }
-    // scores
+    // this tile's registers are free: fetch the wave's next tile into them
+    if (prefetch) load_tile(tile + nw, kr, vr);
+    lds_wave_sync();
+    // scores: A = K rows 16*blk + lo, chunk 4*ks + hi, from LDS
+    u32x4_t kop[2][C::kSteps];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int ks = 0; ks < C::kSteps; ++ks)
+        kop[blk][ks] = *reinterpret_cast<const u32x4_t*>(myk + (16 * blk + lo) * (D * 2) +
+                                                         (((4 * ks + hi) ^ kswz<D>(16 * blk + lo)) << 4));
     f32x4_t sacc[NHB][2];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
@@ -338,11 +357,9 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
         f32x4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < C::kSteps; ++ks)
-          a = mfma16<DT>(kr[blk][ks], qop[hb][ks], a);
+          a = mfma16<DT>(kop[blk][ks], qop[hb][ks], a);
         sacc[hb][blk] = a;
       }
-    // this tile's registers are free: fetch the wave's next tile into them
-    if (prefetch) load_tile(tile + nw, kr, vr);
 
     // online softmax; lane holds keys 16*blk + 4*hi + r of the tile, head lo
     const int rel0 = tile * kKT + 4 * hi;
@@ -410,18 +427,14 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int ks = 0; ks < C::kSteps; ++ks) {
-          u32x4_t w = {0u, 0u, 0u, 0u};
-          if (blk == 0 && lo == 0) w = *reinterpret_cast<const u32x4_t*>(s_new + (4 * ks + hi) * 16);
-          ka[blk][ks] = w;
-        }
-#pragma unroll
       for (int t = 0; t < C::kVLoads; ++t) {
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (t == 0 && lane < C::kChunks) w = *reinterpret_cast<const u32x4_t*>(s_new + D * 2 + lane * 16);
-        va[t] = w;
+        u32x4_t wk = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
+        if (t == 0 && lane < C::kChunks) {
+          wk = *reinterpret_cast<const u32x4_t*>(s_new + lane * 16);
+          wv = *reinterpret_cast<const u32x4_t*>(s_new + D * 2 + lane * 16);
+        }
+        ka[t] = wk;
+        va[t] = wv;
       }
       process(0, ka, va, 1, false);
     }
