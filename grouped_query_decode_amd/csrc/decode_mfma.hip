@@ -27,18 +27,19 @@
 // Each wave walks its own 32-position tiles of the split (tile t goes to wave
 // t mod waves) with one tile in flight: the next tile's loads go out as soon
 // as this tile's K and V rows are in LDS, and land during its scores, softmax
-// and weighted sum (two tiles in flight per wave measured ~5% slower: the
-// extra requests in the memory system cost more than the latency they hide;
-// K loaded straight into the MFMA's register layout -- 64 bytes of each of
-// 16 rows per instruction instead of 1 KB of contiguous rows -- 2-6% slower).  The waves merge (max, sum, output)
-// through LDS.  With several splits, each
-// workgroup writes its partial (max, sum, output) per head; the last workgroup
-// of a (b, g) to finish -- found with a counter in the workspace header, which
-// it resets -- merges the partials (log-sum-exp) and writes the output, so one
-// launch does the whole step.  Positions at or beyond the sequence length are
-// never loaded (the buffer loads end there and return zeros): their K rows are
-// zero, their scores are set to -inf before the softmax and their V rows are
-// zero, so cache contents there (NaN included) cannot reach the arithmetic.
+// and weighted sum.  (Two tiles in flight per wave measured ~5% slower: the
+// extra requests in the memory system cost more than the latency they hide.
+// K loaded straight into the MFMA's register layout -- 64 bytes of each of 16
+// rows per load instruction instead of 1 KB of contiguous rows -- measured
+// 2-6% slower.)  The waves merge (max, sum, output) through LDS.  With several
+// splits, each workgroup writes its partial (max, sum, output) per head; the
+// last workgroup of a (b, g) to finish -- found with a counter in the
+// workspace header, which it resets -- merges the partials (log-sum-exp) and
+// writes the output, so one launch does the whole step.  Positions at or
+// beyond the sequence length are never loaded (the buffer loads end there and
+// return zeros): their K rows are zero, their scores are set to -inf before
+// the softmax and their V rows are zero, so cache contents there (NaN
+// included) cannot reach the arithmetic.
 
 #include "device_common.h"
 #include "internal.h"
@@ -54,7 +55,7 @@ struct Cfg {
   static constexpr int kSteps = D / 32;           // MFMA k-steps over the head dimension
   static constexpr int kColBlocks = D / 16;       // 16-wide output column blocks
   static constexpr int kChunks = D / 8;           // 16-byte chunks per cached row
-  static constexpr int kVLoads = kKT * kChunks / 64;
+  static constexpr int kTileLoads = kKT * kChunks / 64;   // 64-lane 16-byte loads per K or V tile
   static constexpr int kPitch = D * 2 + 32;       // LDS bytes per V row (transposing reads hit distinct banks)
   static constexpr int kKBytes = kKT * D * 2;     // LDS bytes per K tile (rows unpadded, chunks permuted)
   static constexpr int kWaveLds = kKT * kPitch + kKBytes;
@@ -304,17 +305,17 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   // K and V rows land 16 bytes per lane, each 64-lane load covering 64 /
   // kChunks whole rows (1 KB of contiguous cache), and go through the wave's
   // LDS area: K in the score MFMA's A layout, V for the transposing reads.
-  const int v_lane = lane * 16;
-  typedef u32x4_t KTile[C::kVLoads];
-  typedef u32x4_t VTile[C::kVLoads];
+  const int row_lane = lane * 16;
+  typedef u32x4_t KTile[C::kTileLoads];
+  typedef u32x4_t VTile[C::kTileLoads];
   auto load_tile = [&](int tile, KTile& kr, VTile& vr) {
     const int base = tile * (kKT * D * 2);
 #pragma unroll
-    for (int t = 0; t < C::kVLoads; ++t)
-      kr[t] = __builtin_amdgcn_raw_buffer_load_b128(rk, base + v_lane + t * 1024, 0, 0);
+    for (int t = 0; t < C::kTileLoads; ++t)
+      kr[t] = __builtin_amdgcn_raw_buffer_load_b128(rk, base + row_lane + t * 1024, 0, 0);
 #pragma unroll
-    for (int t = 0; t < C::kVLoads; ++t)
-      vr[t] = __builtin_amdgcn_raw_buffer_load_b128(rv, base + v_lane + t * 1024, 0, kNonTemporal);
+    for (int t = 0; t < C::kTileLoads; ++t)
+      vr[t] = __builtin_amdgcn_raw_buffer_load_b128(rv, base + row_lane + t * 1024, 0, kNonTemporal);
     // keep each tile's loads together and in program order, so that the
     // wait before a tile's use covers just the loads issued before it
     __builtin_amdgcn_sched_barrier(0);
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
     // position c ^ kswz(r) (unpadded rows; the A-operand reads below then hit
     // every bank once per 16 lanes), and V rows (padded rows)
 #pragma unroll
-    for (int t = 0; t < C::kVLoads; ++t) {
+    for (int t = 0; t < C::kTileLoads; ++t) {
       const int idx = t * 64 + lane;
       const int r = idx / C::kChunks, c = idx % C::kChunks;
       *reinterpret_cast<u32x4_t*>(myk + r * (D * 2) + ((c ^ kswz<D>(r)) << 4)) = kr[t];
@@ -427,7 +428,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-      for (int t = 0; t < C::kVLoads; ++t) {
+      for (int t = 0; t < C::kTileLoads; ++t) {
         u32x4_t wk = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
         if (t == 0 && lane < C::kChunks) {
           wk = *reinterpret_cast<const u32x4_t*>(s_new + lane * 16);

@@ -206,7 +206,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_mfma_kernel(PrefillPr
   u32x4_t qop[C::kSteps];
   {
     const bool rvq = t_row < p.T;
-    const uint16_t* qrow = p.q + ((int64_t(b) * p.T + (rvq ? t_row : 0)) * p.hm.q_heads + p.hm.q_head(g, q_valid ? qr : p.n_rep - 1)) * D;
+    const uint16_t* qrow = p.q + ((int64_t(b) * p.T + (rvq ? t_row : 0)) * p.hm.q_heads +
+                                  p.hm.q_head(g, q_valid ? qr : p.n_rep - 1)) * D;
 #pragma unroll
     for (int ks = 0; ks < C::kSteps; ++ks) {
       u32x4_t w = {0u, 0u, 0u, 0u};
