@@ -526,6 +526,38 @@ def bench_meanpool(torch, gqa, synth, warmup, reps, means, key, keep_sample=Fals
     return res, sample
 
 
+def bench_meanpool_batch(torch, gqa, synth, count, warmup, reps, means, key):
+    """kv_meanpool_heads_batch over `count` T5-XXL projections per call (count
+    = 2: one layer's K and V; 16: eight layers'), timed per call; the rate
+    and roofline count every projection's bytes."""
+    w = synth.WORKLOADS["t5xxl_meanpool_bf16"]
+    per_head = 1
+    for s in w.per_head_shape:
+        per_head *= s
+    in_bytes = w.H * per_head * 2
+    R = max(1, min(256, math.ceil((1 << 30) / (count * in_bytes))))
+    reps_in = [[synth.meanpool_inputs(w.H, w.per_head_shape, dtype=w.dtype, seed=1000 * r + j, device=DEV)["w"]
+                for j in range(count)] for r in range(R)]
+    outs = [torch.empty((w.G,) + tuple(w.per_head_shape), dtype=reps_in[0][0].dtype, device=DEV)
+            for _ in range(count)]
+
+    def call(i):
+        gqa.meanpool_heads_batch(reps_in[i % R], w.G, outs=outs)
+
+    t = graph_time(torch, call, calls_for(_eager_ms(torch, call, 20)), warmup, reps=reps, out=outs[-1])
+    nbytes = count * (w.H + w.G) * per_head * 2
+    gbps = round(nbytes / (t["median_ms"] * 1e-3) / 1e9, 1)
+    res = {"H": w.H, "G": w.G, "per_head_shape": list(w.per_head_shape), "projections_per_call": count,
+           "replicas": R}
+    _finish_timing(res, t)
+    res.update({"us_per_projection": round(t["median_ms"] * 1e3 / count, 3), "bytes_per_call": nbytes,
+                "GBps": gbps, "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                "roofline": _roofline_hbm(gbps, "meanpool_vec8_kernel", nbytes, key, means)})
+    del reps_in
+    torch.cuda.empty_cache()
+    return res
+
+
 def g_sweep_fit(points):
     """Least-squares line time = fixed + bytes / bandwidth over the G sweep."""
     xs = [p["bytes_per_call"] for p in points]
@@ -889,6 +921,9 @@ def main():
                                                         "t5xxl_meanpool", keep_sample=want_cpu)
         if s:
             samples.append(s)
+    for count, k in ((2, "t5xxl_meanpool_kv_layer"), (16, "t5xxl_meanpool_8_layers_kv")):
+        if run(k):
+            secondary[k] = bench_meanpool_batch(torch, gqa, synth, count, args.warmup, reps, means, k)
     # prefill runs the matrix cores flat out: its first ~20 calls after the
     # memory-bound work run ~20% slower while the clock ramps up, so it gets
     # PREFILL_WARMUP untimed calls (about 35 ms) first

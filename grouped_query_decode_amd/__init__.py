@@ -14,6 +14,7 @@ library is missing, every call raises.
     gqkva_decode(q, k_cache, v_cache, seqlens)  # all query-group x K/V-group pairs
     gqkva_prefill_causal(q, k, v)
     meanpool_heads(w, G)                        # MHA -> GQA K/V conversion
+    meanpool_heads_batch([wk, wv], G)           # several projections per launch
 """
 
 from __future__ import annotations
@@ -28,7 +29,7 @@ __all__ = [
     "GQAError", "library_path", "load_library", "decode", "decode_append", "decode_noalloc",
     "decode_num_splits",
     "decode_workspace_bytes", "prefill_causal", "prefill_chunk", "gqkva_decode",
-    "gqkva_prefill_causal", "meanpool_heads", "DTYPE_CODES",
+    "gqkva_prefill_causal", "meanpool_heads", "meanpool_heads_batch", "DTYPE_CODES",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -90,6 +91,8 @@ def load_library():
     lib.gqkva_prefill_causal.restype = i32
     lib.kv_meanpool_heads.argtypes = [vp, vp, i32, i32, i64, i32, vp]
     lib.kv_meanpool_heads.restype = i32
+    lib.kv_meanpool_heads_batch.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, i32, i64, i32, vp]
+    lib.kv_meanpool_heads_batch.restype = i32
     lib.gqa_status_string.argtypes = [i32]
     lib.gqa_status_string.restype = ctypes.c_char_p
     lib.gqa_last_error.argtypes = []
@@ -433,3 +436,41 @@ def meanpool_heads(w: torch.Tensor, G: int, out: torch.Tensor | None = None) -> 
                                ctypes.c_void_p(_stream_handle(w.device)))
     _check("kv_meanpool_heads", st)
     return out
+
+
+MEANPOOL_MAX_BATCH = 16
+
+
+def meanpool_heads_batch(ws: list, G: int, outs: list | None = None) -> list:
+    """kv_meanpool_heads_batch: several projections of one shape and dtype
+    (e.g. a layer's K and V weights), each [H, ...] -> [G, ...], in one launch
+    per MEANPOOL_MAX_BATCH projections."""
+    lib = load_library()
+    if not ws:
+        return []
+    w0 = ws[0]
+    if w0.dim() < 1:
+        raise ValueError("w must have a leading head dimension")
+    for w in ws:
+        if w.shape != w0.shape or w.dtype != w0.dtype:
+            raise ValueError("every projection must have the first one's shape and dtype")
+        _require_device("w", w, w0.device)
+    H = w0.shape[0]
+    per_head = w0[0].numel() if H > 0 else 0
+    if outs is None:
+        outs = [torch.empty((G,) + tuple(w0.shape[1:]), dtype=w0.dtype, device=w0.device) for _ in ws]
+    elif len(outs) != len(ws):
+        raise ValueError("one output per projection")
+    for o in outs:
+        _require_device("out", o, w0.device)
+        if o.shape != (G,) + tuple(w0.shape[1:]) or o.dtype != w0.dtype:
+            raise ValueError("out must be [G, ...] in w's dtype")
+    for i in range(0, len(ws), MEANPOOL_MAX_BATCH):
+        chunk_in, chunk_out = ws[i:i + MEANPOOL_MAX_BATCH], outs[i:i + MEANPOOL_MAX_BATCH]
+        n = len(chunk_in)
+        arr_in = (ctypes.c_void_p * n)(*[w.data_ptr() for w in chunk_in])
+        arr_out = (ctypes.c_void_p * n)(*[o.data_ptr() for o in chunk_out])
+        st = lib.kv_meanpool_heads_batch(arr_in, arr_out, n, H, G, per_head, _dtype_code(w0),
+                                         ctypes.c_void_p(_stream_handle(w0.device)))
+        _check("kv_meanpool_heads_batch", st)
+    return outs

@@ -451,28 +451,46 @@ size_t gqkva_decode_workspace_bytes(int B, int g_q, int g_kv, int d, int n_max, 
   return workspace_for(B, g_q * g_kv, d, S);
 }
 
-gqa_status kv_meanpool_heads(const void* w_in, void* w_out, int H, int G, int64_t per_head_elems,
-                             gqa_dtype dtype, void* stream_v) {
+static_assert(gqa::kMaxMeanpoolBatch == GQA_MEANPOOL_MAX_BATCH, "one batch limit");
+
+gqa_status kv_meanpool_heads_batch(const void* const* w_in, void* const* w_out, int count, int H, int G,
+                                   int64_t per_head_elems, gqa_dtype dtype, void* stream_v) {
   g_last_error.clear();
   if (!known_dtype(dtype))
     return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: unknown dtype %d", dtype);
+  if (count < 0 || count > GQA_MEANPOOL_MAX_BATCH)
+    return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads_batch: count=%d (0 .. %d)", count,
+                GQA_MEANPOOL_MAX_BATCH);
   if (H < 1 || G < 1 || H % G != 0)
     return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: H=%d must be a positive multiple of G=%d",
                 H, G);
   if (per_head_elems < 0)
     return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: per_head_elems=%lld",
                 (long long)per_head_elems);
-  if (per_head_elems == 0) return ok();
-  if (!w_in || !w_out) return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: NULL tensor");
-  if (!aligned16(w_in) || !aligned16(w_out))
-    return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: tensors must be 16-byte aligned");
+  if (per_head_elems == 0 || count == 0) return ok();
+  if (!w_in || !w_out) return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads_batch: NULL pointer array");
+  for (int j = 0; j < count; ++j) {
+    if (!w_in[j] || !w_out[j]) return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: NULL tensor (projection %d)", j);
+    if (!aligned16(w_in[j]) || !aligned16(w_out[j]))
+      return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: tensors must be 16-byte aligned (projection %d)", j);
+  }
   if (int64_t(H) * per_head_elems > (int64_t(1) << 40))
     return fail(GQA_ERR_INVALID_ARG, "kv_meanpool_heads: problem too large");
   auto p = gqa::problem_for<gqa::MeanpoolProblem>();
-  p.w_in = w_in; p.w_out = w_out; p.H = H; p.G = G; p.n_rep = H / G;
+  for (int j = 0; j < gqa::kMaxMeanpoolBatch; ++j) {
+    p.w_in[j] = j < count ? w_in[j] : nullptr;
+    p.w_out[j] = j < count ? w_out[j] : nullptr;
+  }
+  p.count = count;
+  p.H = H; p.G = G; p.n_rep = H / G;
   p.per_head_elems = per_head_elems; p.dtype = dtype;
   return launched(gqa::launch_meanpool(p, static_cast<hipStream_t>(stream_v)),
                   "kv_meanpool_heads");
+}
+
+gqa_status kv_meanpool_heads(const void* w_in, void* w_out, int H, int G, int64_t per_head_elems,
+                             gqa_dtype dtype, void* stream_v) {
+  return kv_meanpool_heads_batch(&w_in, &w_out, 1, H, G, per_head_elems, dtype, stream_v);
 }
 
 const char* gqa_status_string(int status) {

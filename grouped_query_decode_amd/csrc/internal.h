@@ -141,10 +141,12 @@ struct AppendProblem {
   int row_bytes;            // d * itemsize, a multiple of 16
 };
 
+constexpr int kMaxMeanpoolBatch = 16;   // projections per launch (GQA_MEANPOOL_MAX_BATCH)
 struct MeanpoolProblem {
   uint32_t abi_bytes;        // sizeof(MeanpoolProblem) where it was filled in (see problem_for)
-  const void* w_in;
-  void* w_out;
+  const void* w_in[kMaxMeanpoolBatch];   // projection j's input and output (j < count)
+  void* w_out[kMaxMeanpoolBatch];
+  int count;
   int H, G, n_rep;
   int64_t per_head_elems;
   int dtype;

@@ -11,6 +11,8 @@
 // element is read once), sums in float32 in head order, divides once
 // (correctly rounded) and rounds once to the storage type.  A grid-stride loop
 // covers the output; a scalar kernel handles sizes that are not a multiple of 8.
+// Several projections of one shape can go in one launch (grid row y =
+// projection y): the launch's fixed cost is then paid once for all of them.
 
 #include "device_common.h"
 #include "internal.h"
@@ -22,12 +24,13 @@ namespace {
 // are issued before the first add, so NB requests per thread are in flight;
 // the adds run in head order (the same rounding as one head at a time).
 template <int DT, int NB>
-__device__ __forceinline__ void add_heads(const MeanpoolProblem& p, int64_t g, int64_t e8, int k0, float* acc) {
+__device__ __forceinline__ void add_heads(const MeanpoolProblem& p, const void* w_in, int64_t g, int64_t e8, int k0,
+                                          float* acc) {
   if constexpr (DT != kF32) {
     u32x4_t w[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      w[j] = ld16_stream(static_cast<const uint16_t*>(p.w_in) + (g * p.n_rep + k0 + j) * p.per_head_elems + e8 * 8);
+      w[j] = ld16_stream(static_cast<const uint16_t*>(w_in) + (g * p.n_rep + k0 + j) * p.per_head_elems + e8 * 8);
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -39,7 +42,7 @@ __device__ __forceinline__ void add_heads(const MeanpoolProblem& p, int64_t g, i
     u32x4_t a[NB], b[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const float* src = static_cast<const float*>(p.w_in) + (g * p.n_rep + k0 + j) * p.per_head_elems + e8 * 8;
+      const float* src = static_cast<const float*>(w_in) + (g * p.n_rep + k0 + j) * p.per_head_elems + e8 * 8;
       a[j] = ld16_stream(src);
       b[j] = ld16_stream(src + 4);
     }
@@ -55,6 +58,8 @@ __device__ __forceinline__ void add_heads(const MeanpoolProblem& p, int64_t g, i
 
 template <int DT>
 __global__ __launch_bounds__(256) void meanpool_vec8_kernel(MeanpoolProblem p) {
+  const void* w_in = p.w_in[blockIdx.y];
+  void* w_out = p.w_out[blockIdx.y];
   const int64_t vec_per_head = p.per_head_elems / 8;
   const int64_t total = int64_t(p.G) * vec_per_head;
   const float n = float(p.n_rep);
@@ -64,18 +69,18 @@ __global__ __launch_bounds__(256) void meanpool_vec8_kernel(MeanpoolProblem p) {
     const int64_t e8 = i - g * vec_per_head;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int k = 0;
-    for (; k + 8 <= p.n_rep; k += 8) add_heads<DT, 8>(p, g, e8, k, acc);
+    for (; k + 8 <= p.n_rep; k += 8) add_heads<DT, 8>(p, w_in, g, e8, k, acc);
     if (k + 4 <= p.n_rep) {
-      add_heads<DT, 4>(p, g, e8, k, acc);
+      add_heads<DT, 4>(p, w_in, g, e8, k, acc);
       k += 4;
     }
-    for (; k < p.n_rep; ++k) add_heads<DT, 1>(p, g, e8, k, acc);
+    for (; k < p.n_rep; ++k) add_heads<DT, 1>(p, w_in, g, e8, k, acc);
     const int64_t oel = g * p.per_head_elems + e8 * 8;
     if constexpr (DT != kF32) {
       u32x4_t w;
 #pragma unroll
       for (int t = 0; t < 4; ++t) w[t] = Half16<DT>::pack2(acc[2 * t] / n, acc[2 * t + 1] / n);
-      st16(static_cast<uint16_t*>(p.w_out) + oel, w);
+      st16(static_cast<uint16_t*>(w_out) + oel, w);
     } else {
       u32x4_t a, b;
 #pragma unroll
@@ -83,7 +88,7 @@ __global__ __launch_bounds__(256) void meanpool_vec8_kernel(MeanpoolProblem p) {
         a[t] = __float_as_uint(acc[t] / n);
         b[t] = __float_as_uint(acc[4 + t] / n);
       }
-      float* dst = static_cast<float*>(p.w_out) + oel;
+      float* dst = static_cast<float*>(w_out) + oel;
       st16(dst, a);
       st16(dst + 4, b);
     }
@@ -92,6 +97,8 @@ __global__ __launch_bounds__(256) void meanpool_vec8_kernel(MeanpoolProblem p) {
 
 template <int DT>
 __global__ __launch_bounds__(256) void meanpool_scalar_kernel(MeanpoolProblem p) {
+  const void* w_in = p.w_in[blockIdx.y];
+  void* w_out = p.w_out[blockIdx.y];
   const int64_t total = int64_t(p.G) * p.per_head_elems;
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
        i += int64_t(gridDim.x) * blockDim.x) {
@@ -101,15 +108,15 @@ __global__ __launch_bounds__(256) void meanpool_scalar_kernel(MeanpoolProblem p)
     for (int k = 0; k < p.n_rep; ++k) {
       const int64_t elem = (g * p.n_rep + k) * p.per_head_elems + e;
       if constexpr (DT == kF32)
-        acc += static_cast<const float*>(p.w_in)[elem];
+        acc += static_cast<const float*>(w_in)[elem];
       else
-        acc += Half16<DT>::lo(static_cast<const uint16_t*>(p.w_in)[elem]);
+        acc += Half16<DT>::lo(static_cast<const uint16_t*>(w_in)[elem]);
     }
     const float mean = acc / float(p.n_rep);
     if constexpr (DT == kF32)
-      static_cast<float*>(p.w_out)[i] = mean;
+      static_cast<float*>(w_out)[i] = mean;
     else
-      static_cast<uint16_t*>(p.w_out)[i] = uint16_t(Half16<DT>::pack2(mean, 0.f) & 0xffffu);
+      static_cast<uint16_t*>(w_out)[i] = uint16_t(Half16<DT>::pack2(mean, 0.f) & 0xffffu);
   }
 }
 
@@ -119,11 +126,13 @@ hipError_t launch_meanpool(const MeanpoolProblem& p, hipStream_t stream) {
   if (!abi_ok(p)) return kAbiMismatch;
   const bool vec = (p.per_head_elems % 8) == 0;
   const int64_t work = vec ? int64_t(p.G) * (p.per_head_elems / 8) : int64_t(p.G) * p.per_head_elems;
-  // enough threads to cover the output once, capped (grid-stride beyond)
+  if (p.count < 1 || p.count > kMaxMeanpoolBatch) return hipErrorInvalidValue;
+  // enough threads to cover each projection's output once, capped (grid-stride
+  // beyond); grid row y is projection y
   int64_t blocks = (work + 255) / 256;
   if (blocks > 256 * 64) blocks = 256 * 64;
   if (blocks < 1) blocks = 1;
-  const dim3 grid = dim3(unsigned(blocks)), block = dim3(256);
+  const dim3 grid = dim3(unsigned(blocks), unsigned(p.count)), block = dim3(256);
   if (vec) {
     if (p.dtype == kBF16)
       hipLaunchKernelGGL(meanpool_vec8_kernel<kBF16>, grid, block, 0, stream, p);

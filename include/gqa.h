@@ -276,6 +276,26 @@ gqa_status kv_meanpool_heads(const void* w_in, void* w_out, int H, int G,
                              int64_t per_head_elems, gqa_dtype dtype, void* stream);
 
 /*
+ * kv_meanpool_heads_batch - kv_meanpool_heads over up to
+ * GQA_MEANPOOL_MAX_BATCH projections of one shape in a single launch (e.g. the
+ * key and value projections of one or several layers, as a checkpoint
+ * conversion needs them): projection j reads w_in[j] and writes w_out[j],
+ * with exactly the arithmetic and results of kv_meanpool_heads on that pair;
+ * one launch pays the fixed cost once.
+ *
+ *   w_in, w_out  host arrays of `count` device pointers (the arrays are read
+ *                during the call only; the pointed-to tensors must not
+ *                overlap between an input and any output)
+ *   count        0 .. GQA_MEANPOOL_MAX_BATCH (0: a valid no-op)
+ *
+ * Errors: as kv_meanpool_heads, plus GQA_ERR_INVALID_ARG for a count out of
+ * range, a NULL array or a NULL/misaligned pointer in it.
+ */
+#define GQA_MEANPOOL_MAX_BATCH 16
+gqa_status kv_meanpool_heads_batch(const void* const* w_in, void* const* w_out, int count, int H,
+                                   int G, int64_t per_head_elems, gqa_dtype dtype, void* stream);
+
+/*
  * gqa_decode_noalloc - gqa_decode_split for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc): the same computation, kernels and results, with the

@@ -36,7 +36,7 @@ def test_header_declares_the_api():
     names = declared_functions()
     for n in ("gqa_decode", "gqa_decode_split", "gqa_decode_append", "gqa_prefill_causal",
               "gqa_prefill_chunk", "gqkva_decode", "gqkva_decode_workspace_bytes",
-              "gqkva_prefill_causal", "kv_meanpool_heads",
+              "gqkva_prefill_causal", "kv_meanpool_heads", "kv_meanpool_heads_batch",
               "gqa_decode_workspace_bytes", "gqa_decode_num_splits", "gqa_status_string",
               "gqa_last_error", "gqa_version", "gqa_decode_noalloc"):
         assert n in names, n
@@ -176,6 +176,26 @@ def test_meanpool_rejects_bad_arguments(lib):
     assert call(o=P_MIS) == INVALID
     assert call(dt=5) == INVALID
     assert call(w=ctypes.c_void_p(0), o=ctypes.c_void_p(0), n=0) == OK
+
+
+def test_meanpool_batch_rejects_bad_arguments(lib):
+    def arr(*ptrs):
+        return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+    def call(ws=None, os_=None, count=2, H=64, G=8, n=4096 * 64, dt=BF16):
+        ws = arr(P, P) if ws is None else ws
+        os_ = arr(P, P) if os_ is None else os_
+        return lib.kv_meanpool_heads_batch(ws, os_, count, H, G, n, dt, None)
+    assert call(count=-1) == INVALID
+    assert call(count=17) == INVALID            # beyond GQA_MEANPOOL_MAX_BATCH
+    assert call(G=3) == INVALID
+    assert call(ws=arr(P, ctypes.c_void_p(0))) == INVALID
+    assert call(os_=arr(P, P_MIS)) == INVALID
+    assert call(ws=None, count=2, dt=5) == INVALID
+    assert lib.kv_meanpool_heads_batch(None, None, 2, 64, 8, 4096, BF16, None) == INVALID
+    # count 0 and empty heads are valid no-ops (nothing is read)
+    assert lib.kv_meanpool_heads_batch(None, None, 0, 64, 8, 4096, BF16, None) == OK
+    assert call(ws=arr(ctypes.c_void_p(0), ctypes.c_void_p(0)), n=0) == OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

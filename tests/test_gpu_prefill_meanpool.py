@@ -218,6 +218,35 @@ def test_meanpool_cases(H, G, shape, dt):
         assert torch.equal(out, w)
 
 
+@pytest.mark.parametrize("count,H,G,shape,dt", [
+    (2, 64, 8, (4096, 64), "bf16"),          # one T5-XXL layer's K and V projections
+    (16, 8, 2, (16, 64), "f32"),             # a full batch
+    (17, 6, 3, (7, 5), "bf16"),              # one batch of 16 and one of 1; odd size (scalar kernel)
+    (3, 32, 4, (13, 8), "f16"),
+    (1, 8, 8, (5, 3), "bf16"),
+])
+def test_meanpool_batch_matches_single_calls(count, H, G, shape, dt):
+    """kv_meanpool_heads_batch: every projection bit-identical to its own
+    kv_meanpool_heads call, and within the single call's bound of the oracle."""
+    announce(f"meanpool batch count={count} H={H} G={G} shape={shape} {dt}")
+    ws = [synth.meanpool_inputs(H, shape, dtype=dt, seed=100 + j, device=DEV)["w"] for j in range(count)]
+    outs = gqa.meanpool_heads_batch(ws, G)
+    torch.cuda.synchronize()
+    assert len(outs) == count
+    for w, out in zip(ws, outs):
+        single = _meanpool(w, G)
+        assert torch.equal(out.view(torch.uint8), single.view(torch.uint8))
+        ref = oracle.meanpool_ref(to64(w), G)
+        if dt == "f32":
+            assert np.abs(to64(out) - ref).max() <= 1e-5
+        elif dt == "bf16":
+            assert bf16_ulp_distance(out, ref).max() <= 1
+        else:   # within one fp16 ulp of the oracle rounded to nearest even
+            got = out.cpu().numpy().view(np.int16).astype(np.int64)
+            want = ref.astype(np.float16).view(np.int16).astype(np.int64)
+            assert np.abs(got - want).max() <= 1
+
+
 def test_meanpool_identical_heads_bit_exact():
     announce("meanpool identical heads")
     base = synth.meanpool_inputs(1, (512, 64), dtype="bf16", seed=3, device=DEV)["w"]
