@@ -248,6 +248,34 @@ class ReadProbe:
             res[name] = {"ns_per_wave_instruction_per_simd": round(ms * 1e6 / wi, 4)}
         return res
 
+    def lds_rates(self, blocks=512):
+        """LDS cycles per wave instruction per compute unit (ds_read_b128, and ds_read_b64_tr_b16 at
+        the causal prefill's V^T addresses), at the clock the chip reports for the run."""
+        torch = self.torch
+        lib = self.lib
+        lib.gqa_probe_lds_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        lib.gqa_probe_lds_rate.restype = ctypes.c_int
+        stream = torch.cuda.current_stream()
+        res = {}
+        for kind, name, lane_bytes in ((0, "ds_read_b128", 16), (1, "ds_read_b64_tr_b16_prefill_vt", 8)):
+            call = lambda: lib.gqa_probe_lds_rate(ctypes.c_void_p(self.sink.data_ptr()), kind, blocks,  # noqa: E731
+                                                  ctypes.c_void_p(stream.cuda_stream))
+            if call() != 0:
+                raise RuntimeError("gqa_probe_lds_rate refused its launch")
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(5):
+                call()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / 5
+            # wave-instructions per CU: blocks x 4 waves / 256 CUs x 4096 steps x 8
+            wi = blocks * 4 / 256 * 4096 * 8
+            res[name] = {"ns_per_wave_instruction_per_cu": round(ms * 1e6 / wi, 4),
+                         "bytes_per_ns_per_cu": round(64 * lane_bytes * wi / (ms * 1e6), 1)}
+        return res
+
     def read(self, buf, blocks, unroll):
         rc = self.lib.gqa_probe_hbm_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
                                          ctypes.c_void_p(self.sink.data_ptr()), blocks, unroll,
@@ -833,7 +861,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=8.0)
     ap.add_argument("--probe-rates", action="store_true",
-                    help="print the vector-unit issue rates (fma, exp) and exit")
+                    help="print the vector-unit issue rates (fma, exp) and LDS read rates, and exit")
     ap.add_argument("--timeline", action="store_true",
                     help="print per-workgroup decode phase timings (libgqa_timeline.so) instead of the bench line")
     ap.add_argument("--min-rep-ms", type=float, default=50.0,
@@ -859,7 +887,8 @@ def main():
         return
     probe = ReadProbe(torch)
     if args.probe_rates:
-        print(json.dumps({"valu_issue_rates": probe.valu_rates()}), flush=True)
+        print(json.dumps({"valu_issue_rates": probe.valu_rates(), "lds_read_rates": probe.lds_rates()}),
+              flush=True)
         return
     flusher = ColdFlusher(torch, probe)
     means = stored_kernel_means()

@@ -108,3 +108,70 @@ extern "C" int gqa_probe_valu_rate(float* out, int kind, int blocks, void* strea
     hipLaunchKernelGGL(valu_rate_kernel<2>, dim3(unsigned(blocks)), dim3(kThreads), 0, s, out, 0.001f);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
+
+// ---------------------------------------------------------------------------
+// LDS read rates: 256-thread workgroups, each filling a 64 KB LDS array and
+// then reading it 4096 x 8 times per lane (two workgroups, 8 waves, per CU).
+// Kind 0: ds_read_b128, lane l of a wave at 16 l bytes past a per-wave base
+// (every 16-lane quarter covers the 64 banks once).  Kind 1:
+// ds_read_b64_tr_b16 at the addresses the causal prefill reads its V^T
+// operand from (128-dim bf16 rows of 256 bytes, 16-byte chunks permuted by
+// XOR with 64 x the 64-dim block; see the prefill kernel), the 8 reads per
+// step alternating between two 16 KB halves.  Addresses are precomputed, so
+// the loop is the reads and one XOR each.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kLdsBytes = 65536;
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void lds_rate_kernel(uint32_t* sink, uint32_t key) {
+  __shared__ __attribute__((aligned(16))) char tile[kLdsBytes];
+  for (int i = threadIdx.x; i < kLdsBytes / 16; i += kThreads)
+    reinterpret_cast<u32x4_t*>(tile)[i] = u32x4_t{uint32_t(i), 3u * uint32_t(i), 5u, 7u};
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  if constexpr (KIND == 0) {
+    int off = wave * 4096 + lane * 16;
+    for (int i = 0; i < kRateSteps; ++i) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        acc ^= *reinterpret_cast<const u32x4_t*>(tile + ((off + u * 1024) & (kLdsBytes - 1)));
+      off = (off + 8192) & (kLdsBytes - 1);
+    }
+  } else {
+    typedef short i16x4_t __attribute__((ext_vector_type(4)));
+    const int l32 = lane & 31, e4 = (l32 >> 2) & 3;
+    const int vx = (4 * (lane >> 5) + e4) * 256 + 64 * e4 + 32 * (l32 >> 4) + 8 * (l32 & 3);
+    int a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] = (vx ^ (64 * (u & 3))) + (u >> 2) * 16 * 256;
+    int half = 0;
+    for (int i = 0; i < kRateSteps; ++i) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(tile + half + a[u]));
+        acc[u & 3] ^= uint32_t(uint16_t(v[0])) ^ (uint32_t(uint16_t(v[1])) << 16) ^ uint32_t(uint16_t(v[2])) ^
+                      (uint32_t(uint16_t(v[3])) << 16);
+      }
+      half ^= 16384;
+    }
+  }
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == key) sink[0] = 1u;
+}
+
+}  // namespace
+
+extern "C" int gqa_probe_lds_rate(uint32_t* sink, int kind, int blocks, void* stream) {
+  if (!sink || (reinterpret_cast<uintptr_t>(sink) & 3u) || blocks < 1 || blocks > (1 << 16) || kind < 0 ||
+      kind > 1)
+    return 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kind == 0)
+    hipLaunchKernelGGL(lds_rate_kernel<0>, dim3(unsigned(blocks)), dim3(kThreads), 0, s, sink, 0x9e3779b9u);
+  else
+    hipLaunchKernelGGL(lds_rate_kernel<1>, dim3(unsigned(blocks)), dim3(kThreads), 0, s, sink, 0x9e3779b9u);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}

@@ -42,6 +42,20 @@ int gqa_probe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int blocks
  */
 int gqa_probe_valu_rate(float* out, int kind, int blocks, void* stream);
 
+/*
+ * gqa_probe_lds_rate - LDS read rate: `blocks` workgroups of 256 threads,
+ * each filling a 64 KB LDS array and reading it with 8 x 4096 instructions
+ * per wave of one kind -- kind 0: ds_read_b128 (16 bytes per lane, each
+ * 16-lane quarter covering the 64 banks once); 1: ds_read_b64_tr_b16 (8
+ * bytes per lane) at the addresses from which the causal prefill kernel reads
+ * its transposed V operand at d = 128.  Two workgroups share a compute unit,
+ * so 512 blocks fill the chip; the launch time gives the LDS cycles per wave
+ * instruction of that kind.  sink: device, 4 bytes, written only if the
+ * folded data equals a fixed key.  Returns 0, 1 for an invalid argument
+ * (nothing enqueued), 4 if the launch was refused.
+ */
+int gqa_probe_lds_rate(uint32_t* sink, int kind, int blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -55,7 +55,7 @@ def test_probe_library_exports_its_header():
         pytest.fail("libgqa_probe.so is not built: run __graft_entry__.build() first")
     raw = ctypes.CDLL(path)
     names = declared_functions(os.path.join(ROOT, "include", "gqa_probe.h"))
-    assert names == ["gqa_probe_hbm_read", "gqa_probe_valu_rate"]
+    assert names == ["gqa_probe_hbm_read", "gqa_probe_lds_rate", "gqa_probe_valu_rate"]
     for name in names:
         assert hasattr(raw, name)
     f = raw.gqa_probe_hbm_read
@@ -74,6 +74,12 @@ def test_probe_library_exports_its_header():
     assert r(P, 3, 1024, None) == 1                       # kind
     assert r(ctypes.c_void_p(0), 0, 1024, None) == 1
     assert r(P, 0, 0, None) == 1
+    lr = raw.gqa_probe_lds_rate
+    lr.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lr.restype = ctypes.c_int
+    assert lr(P, 2, 512, None) == 1                       # kind
+    assert lr(ctypes.c_void_p(0), 0, 512, None) == 1
+    assert lr(P, 1, 0, None) == 1
 
 
 def test_status_strings(lib):
