@@ -130,6 +130,18 @@ def _stream_handle(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _workspace_args(workspace, dev, need: int):
+    """The workspace pointer and size to pass: the caller's (checked to be on the
+    call's GPU), else the cached one when the call needs any."""
+    if workspace is None:
+        if need <= 0:
+            return None, 0
+        workspace = _cached_workspace(dev, need)
+    else:
+        _require_device("workspace", workspace, dev)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
@@ -166,9 +178,11 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlen
     q [B,H,d]; k_cache, v_cache [B,G,Nmax,d]; seqlens [B] int32 (on the GPU).
     ``scale`` defaults to 1/sqrt(d) (as a float32 value).  ``num_splits`` = 0
     lets the library plan the split-N decomposition.  Without ``workspace`` a
-    zero-filled buffer cached per device is used (shared by all calls on that
-    device: calls on different streams that may overlap should each pass
-    their own, zero-filled once).
+    zero-filled buffer cached per (device, current stream) is used, so calls on
+    one stream share it and calls on different streams do not.  A ``workspace``
+    passed in must be a contiguous tensor on q's GPU, zero-filled before its
+    first use (the library leaves it reusable); calls that may overlap must not
+    share one.
     """
     lib = load_library()
     if q.dim() != 3 or k_cache.dim() != 4:
@@ -194,9 +208,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seqlen
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = decode_workspace_bytes(B, H, G, d, n_max, num_splits) if B > 0 else 0
-    if need > 0 and workspace is None:
-        workspace = _cached_workspace(dev, need)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace_args(workspace, dev, need)
     st = lib.gqa_decode_split(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(out),
                               B, H, G, d, n_max, float(scale), _dtype_code(q), int(num_splits),
                               _ptr(workspace), ws_bytes, ctypes.c_void_p(_stream_handle(dev)))
@@ -271,9 +283,7 @@ def decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_c
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = decode_workspace_bytes(B, H, G, d, n_max, num_splits) if B > 0 else 0
-    if need > 0 and workspace is None:
-        workspace = _cached_workspace(dev, need)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace_args(workspace, dev, need)
     st = lib.gqa_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                _ptr(seqlens), _ptr(out), B, H, G, d, n_max, float(scale),
                                _dtype_code(q), int(num_splits), _ptr(workspace), ws_bytes,
@@ -378,9 +388,7 @@ def gqkva_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
         need = lib.gqkva_decode_workspace_bytes(B, g_q, g_kv, d, n_max, num_splits)
         if need == ctypes.c_size_t(-1).value:
             raise ValueError("invalid GQKVA decode shape")
-    if need > 0 and workspace is None:
-        workspace = _cached_workspace(dev, need)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace_args(workspace, dev, need)
     st = lib.gqkva_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(out), B, g_q,
                           g_kv, d, n_max, float(scale), _dtype_code(q), int(num_splits),
                           _ptr(workspace), ws_bytes, ctypes.c_void_p(_stream_handle(dev)))

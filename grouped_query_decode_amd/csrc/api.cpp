@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -276,7 +277,8 @@ gqa_status prefill_impl(const char* name, const void* q, const void* k, const vo
     return fail(GQA_ERR_UNSUPPORTED, "%s: head size d=%d (built for 64 and 128)", name, d);
   const int n_rep = gqkva ? H : H / G;
   const int64_t out_heads = int64_t(G) * n_rep;
-  if (int64_t(B) * T * out_heads * d > (int64_t(1) << 40) ||
+  // (query rows are counted in 32 bits: B*T below 2^31)
+  if (int64_t(B) * T * out_heads * d > (int64_t(1) << 40) || int64_t(B) * T > INT32_MAX ||
       (cache_layout && int64_t(B) * G * n_max * d > (int64_t(1) << 40)))
     return fail(GQA_ERR_INVALID_ARG, "%s: problem too large", name);
   const gqa::HeadMap hm = gqkva ? gqa::gqkva_head_map(H, G) : gqa::gqa_head_map(G, n_rep);

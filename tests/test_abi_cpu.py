@@ -167,6 +167,9 @@ def test_prefill_rejects_bad_arguments(lib):
     assert call(out=P_MIS) == INVALID
     assert call(scale=float("-inf")) == INVALID
     assert call(d=80) == UNSUPPORTED
+    # 2^32 query rows: within the element guard (2^38 elements) but past the
+    # kernels' 32-bit row count
+    assert call(B=65536, T=65536, H=1, G=1, d=64) == INVALID
     z = ctypes.c_void_p(0)
     assert call(q=z, k=z, v=z, out=z, T=0) == OK
     assert call(q=z, k=z, v=z, out=z, B=0) == OK
@@ -217,6 +220,10 @@ def test_binding_rejects_host_tensors(lib):
     k = torch.zeros(1, 2, 16, 64)
     with pytest.raises(ValueError, match="GPU tensor"):
         gqa.decode(q, k, k, torch.zeros(1, dtype=torch.int32))
+    # a caller's workspace is checked like the tensors (never passed on as a host pointer)
+    with pytest.raises(ValueError, match="workspace must be a GPU tensor"):
+        gqa._workspace_args(torch.zeros(1 << 16, dtype=torch.uint8), torch.device("cuda:0"), 4096)
+    assert gqa._workspace_args(None, torch.device("cuda:0"), 0) == (None, 0)
 
 
 def _append(lib, q=P, kn=P, vn=P, k=P, v=P, sl=P, out=P, B=2, H=8, G=2, d=64, n=128, scale=0.125,
