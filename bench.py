@@ -980,7 +980,11 @@ def main():
                 r = v["roofline"]
                 r["frac_of_measured_read_ceiling"] = round(v["GBps"] / ceiling, 4)
                 at = probe_at_size(torch, probe, v["bytes_per_call"], reps, sized)
-                r["read_probe_at_same_bytes"] = {"us": at["us"], "GBps": at["GBps"]}
+                # beyond the probe's 2 GiB buffer the rate no longer depends on size: the
+                # workload's bytes at that rate
+                r["read_probe_at_same_bytes"] = {
+                    "us": round(v["bytes_per_call"] / (at["GBps"] * 1e3), 2), "GBps": at["GBps"],
+                    "bytes_probed": at["bytes"]}
                 r["frac_of_read_probe_at_same_bytes"] = round(v["GBps"] / at["GBps"], 4)
         sized.pop("buf", None)
         torch.cuda.empty_cache()
