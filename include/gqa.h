@@ -317,7 +317,7 @@ gqa_status kv_meanpool_heads_batch(const void* const* w_in, void* const* w_out, 
  * Errors: as gqa_decode_split; GQA_ERR_WORKSPACE when the shape's split
  * partials (gqa_decode_workspace_bytes with the same arguments) exceed
  * GQA_NOALLOC_SCRATCH_BYTES -- e.g. the planner's split of 64 sequences x 32
- * heads x d=128 over 32768 positions needs about 17 MB and fits; lower
+ * heads x d=128 over 32768 positions needs about 12 MB and fits; lower
  * num_splits to fit larger batches.  GQA_ERR_LAUNCH if the set-up fails.
  */
 #define GQA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)

@@ -143,11 +143,11 @@ def test_split_planner_is_host_only_and_consistent(lib):
             assert ws == 65536 + (o_bytes + 255) // 256 * 256 + B * H * S * 2 * 4
         assert ws == lib.gqa_decode_workspace_bytes(B, H, G, d, n, S)
     # long ragged caches are cut into bounded slices
-    assert lib.gqa_decode_num_splits(64, 32, 8, 128, 32768) >= 16
+    assert lib.gqa_decode_num_splits(64, 32, 8, 128, 32768) >= 11
     # about one workgroup per compute unit, splits of at least 128 positions
     planned = {(16, 32, 32, 128, 1024): 1, (16, 32, 8, 128, 1024): 2, (16, 32, 4, 128, 1024): 4,
                (16, 32, 1, 128, 1024): 8, (32, 64, 8, 64, 2048): 1, (1, 8, 2, 64, 128): 1,
-               (64, 32, 8, 128, 32768): 16}
+               (64, 32, 8, 128, 32768): 11}
     for shape, S in planned.items():
         assert lib.gqa_decode_num_splits(*shape) == S, shape
     # forced split counts
