@@ -859,7 +859,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--only", default="", help="comma-separated secondary workload keys")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=8.0)
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--probe-rates", action="store_true",
                     help="print the vector-unit issue rates (fma, exp) and LDS read rates, and exit")
     ap.add_argument("--timeline", action="store_true",
