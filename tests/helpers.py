@@ -69,3 +69,33 @@ def f16_ulp_distance(got_f16: torch.Tensor, ref: np.ndarray) -> np.ndarray:
     a = np.where(a < 0, -(a & 0x7FFF), a)
     b = np.where(b < 0, -(b & 0x7FFF), b)
     return np.abs(a - b)
+
+
+def f32_attention_bound(q, K, V, scale, visible):
+    """First-order forward-error bound of float32 softmax attention, per output
+    element, evaluated with the exact (float64) weights.
+
+    q [R, d]; K, V [n, d]; visible [R, n] (which positions each row attends).
+    A float32 score carries at most gamma_d * |scale| * sum_c |q_c k_c| from
+    its dot product (any summation order), plus a few roundings of the scale,
+    the max subtraction and exp2; a relative error of at most delta on every
+    weight moves the output by at most 2 delta sum_j p_j |v_j - out|, and the
+    float32 weighted sum and its rescalings add gamma_n (sum_j p_j |v_j| + |out|).
+    Returns (exact output, tolerance), both [R, d]."""
+    u = 2.0 ** -24
+    R, d = q.shape
+    n_vis = visible.sum(axis=1)
+    s = scale * (q @ K.T)
+    sabs = abs(scale) * (np.abs(q) @ np.abs(K).T)
+    s = np.where(visible, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    p = np.where(visible, np.exp(s - m), 0.0)
+    p /= p.sum(axis=1, keepdims=True)
+    out = p @ V
+    gd = d * u / (1 - d * u)
+    delta = (gd + 3 * u) * sabs + 2 * u * 1.4426950408889634 * np.abs(np.where(visible, s - m, 0.0)) + 4 * u
+    dmax = np.where(visible, delta, 0.0).max(axis=1)
+    spread = np.einsum("rj,rjc->rc", p, np.abs(V[None, :, :] - out[:, None, :]))
+    gn = n_vis * u / (1 - n_vis * u)
+    tol = 2 * dmax[:, None] * spread + gn[:, None] * (p @ np.abs(V) + np.abs(out)) + 2 * u * np.abs(out)
+    return out, 1.1 * tol + 1e-12

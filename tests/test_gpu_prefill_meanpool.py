@@ -7,7 +7,7 @@ import torch
 import grouped_query_decode_amd as gqa
 import oracle
 import synth
-from helpers import announce, assert_close, bf16_ulp_distance, need_gpu, to64
+from helpers import announce, assert_close, bf16_ulp_distance, f32_attention_bound, need_gpu, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -283,11 +283,10 @@ def test_prefill_random_shapes(case):
     assert_close(out, ref, x["q"].dtype, f"prefill random {case}")
 
 
-# float32 at scale 2: softmax arguments near 100 turn one float32 rounding of
-# a score into a ~1e-5 relative change of its weight, so the float32 bound
-# (set for scale 1/sqrt(d)) cannot hold there; bfloat16 covers that case
+# float32 at scale 2: held to float32's own forward-error bound
+# (f32_attention_bound) rather than the fixed float32 bound set for 1/sqrt(d)
 @pytest.mark.parametrize("scale,dt", [(0.0, "bf16"), (-0.3, "bf16"), (2.0, "bf16"),
-                                      (0.0, "f32"), (-0.3, "f32")])
+                                      (0.0, "f32"), (-0.3, "f32"), (2.0, "f32")])
 def test_prefill_unusual_scales(scale, dt):
     """As for decode: the mean of the visible rows at scale 0, the least similar
     keys favoured at a negative scale, a nearly hard softmax at scale 2."""
@@ -295,4 +294,19 @@ def test_prefill_unusual_scales(scale, dt):
     x = synth.prefill_inputs(1, 300, 8, 2, 128, dtype=dt, seed=19, device=DEV, std=1.0)
     out = _prefill(x, scale)
     ref = oracle.prefill_causal_ref(to64(x["q"]), to64(x["k"]), to64(x["v"]), scale)
+    if dt == "f32" and scale == 2.0:
+        q, k, v = to64(x["q"])[0], to64(x["k"])[0], to64(x["v"])[0]     # [T, H, d], [T, G, d]
+        T, H = q.shape[0], q.shape[1]
+        n_rep = H // k.shape[1]
+        causal = np.tril(np.ones((T, T), dtype=bool))
+        o64 = to64(out)[0]
+        worst = 0.0
+        for h in range(H):
+            exact, tol = f32_attention_bound(q[:, h], k[:, h // n_rep], v[:, h // n_rep], scale, causal)
+            np.testing.assert_allclose(exact, ref[0, :, h], rtol=1e-11, atol=1e-12)
+            err = np.abs(o64[:, h] - ref[0, :, h])
+            assert (err <= tol).all(), (h, float((err / tol).max()))
+            worst = max(worst, float((err / tol).max()))
+        print(f"prefill f32 scale 2: largest error / bound = {worst:.3g}")
+        return
     assert_close(out, ref, x["q"].dtype, f"prefill scale={scale}")
