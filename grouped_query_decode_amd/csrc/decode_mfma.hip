@@ -192,7 +192,7 @@ __device__ __forceinline__ void merge_item(const DecodeProblem& p, const UnitPar
   } while (0)
 #endif
 
-template <int D, int NHB, int DT>
+template <int D, int NHB, int DT, bool APPEND>
 __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(DecodeProblem p) {
   using C = Cfg<D>;
   using H16 = Half16<DT>;
@@ -252,11 +252,11 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   // Append (when k_new is given): the new token's k, v belong in slot
   // raw_len-1 if that slot exists.  The split holding that slot writes them
   // to the cache (the first work group of the K/V head, when several share
-  // it) and attends them straight from a copy in LDS (no workgroup reads that
-  // slot from the cache in this launch); its stream of cached rows stops just
-  // before the slot.
+  // it) and into an LDS copy (lanes of wave 0), from which wave 0 attends them
+  // before its first cached tile (no workgroup reads that slot from the cache
+  // in this launch); its stream of cached rows stops just before the slot.
   __shared__ __attribute__((aligned(16))) char s_new[2 * D * 2];
-  const int p_new = (p.k_new != nullptr && raw_len >= 1 && raw_len <= p.n_max) ? raw_len - 1 : -1;
+  const int p_new = (APPEND && raw_len >= 1 && raw_len <= p.n_max) ? raw_len - 1 : -1;
   const bool owner = p_new >= j0 && p_new < j1;
   if (owner && threadIdx.x < 2 * C::kChunks) {
     const int c = threadIdx.x % C::kChunks;
@@ -418,15 +418,16 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   VTile va;
   int tile = wave;
   load_tile(tile, ka, va);
-  for (; tile < ntiles; tile += nw) {
-    process(tile, ka, va, nvalid, true);
-    if (tile == wave) GQA_PHASE(2);
-  }
-  GQA_PHASE(3);
-  if (owner) {
-    // the appended token, as a one-row tile on wave 0 (its k, v from LDS)
-    __syncthreads();
-    if (wave == 0) {
+  if constexpr (APPEND) {
+    // The appended token first, as a one-row tile on wave 0 (its k, v from
+    // the LDS copy this wave wrote above), while the wave's first cached tile
+    // is still in flight: it then costs nothing on the path after the last
+    // tile.  (Attending it first instead of last changes only the rounding
+    // order of the online softmax.)
+    if (owner && wave == 0) {
+      lds_wave_sync();
+      KTile kn;
+      VTile vn;
 #pragma unroll
       for (int t = 0; t < C::kTileLoads; ++t) {
         u32x4_t wk = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
@@ -434,12 +435,17 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
           wk = *reinterpret_cast<const u32x4_t*>(s_new + lane * 16);
           wv = *reinterpret_cast<const u32x4_t*>(s_new + D * 2 + lane * 16);
         }
-        ka[t] = wk;
-        va[t] = wv;
+        kn[t] = wk;
+        vn[t] = wv;
       }
-      process(0, ka, va, 1, false);
+      process(0, kn, vn, 1, false);
     }
   }
+  for (; tile < ntiles; tile += nw) {
+    process(tile, ka, va, nvalid, true);
+    if (tile == wave) GQA_PHASE(2);
+  }
+  GQA_PHASE(3);
 
   // per-head normaliser: the four lanes of a head hold disjoint positions
 #pragma unroll
@@ -544,7 +550,7 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
 #endif
 }
 
-template <int D, int NHB, int DT>
+template <int D, int NHB, int DT, bool APPEND>
 hipError_t launch_t(const DecodeProblem& p, hipStream_t stream) {
   const int64_t blocks = int64_t(p.B) * (p.G / p.kv_div) * p.num_splits;
   if (blocks <= 0) return hipSuccess;
@@ -552,7 +558,7 @@ hipError_t launch_t(const DecodeProblem& p, hipStream_t stream) {
   // one wave per 32-position tile of a split, at most four
   const int tiles = (p.split_len + kKT - 1) / kKT;
   const int waves = tiles >= 4 ? 4 : (tiles >= 2 ? 2 : 1);
-  hipLaunchKernelGGL((decode_mfma_kernel<D, NHB, DT>), dim3(unsigned(blocks), unsigned(p.kv_div)),
+  hipLaunchKernelGGL((decode_mfma_kernel<D, NHB, DT, APPEND>), dim3(unsigned(blocks), unsigned(p.kv_div)),
                      dim3(64 * waves), 0, stream, p);
   return hipGetLastError();
 }
@@ -569,18 +575,21 @@ bool decode_mfma_supports(int n_rep, int d, int num_splits, int split_len) {
          partials < (int64_t(1) << 31);
 }
 
-template <int DT>
+template <int DT, bool APPEND>
 hipError_t launch_dt(const DecodeProblem& p, hipStream_t stream) {
   if (p.d == 128)
-    return p.n_rep <= 16 ? launch_t<128, 1, DT>(p, stream) : launch_t<128, 2, DT>(p, stream);
-  return p.n_rep <= 16 ? launch_t<64, 1, DT>(p, stream) : launch_t<64, 2, DT>(p, stream);
+    return p.n_rep <= 16 ? launch_t<128, 1, DT, APPEND>(p, stream) : launch_t<128, 2, DT, APPEND>(p, stream);
+  return p.n_rep <= 16 ? launch_t<64, 1, DT, APPEND>(p, stream) : launch_t<64, 2, DT, APPEND>(p, stream);
 }
 
 hipError_t launch_decode_mfma(const DecodeProblem& p, hipStream_t stream) {
   if (!abi_ok(p)) return kAbiMismatch;
   if (p.B <= 0 || p.num_splits <= 0) return hipSuccess;
   if (p.kv_div < 1 || p.G < 1 || p.G % p.kv_div != 0) return hipErrorInvalidValue;
-  return p.dtype == kF16 ? launch_dt<kF16>(p, stream) : launch_dt<kBF16>(p, stream);
+  // the fused append is a variant of its own (the plain decode's code is unchanged by it)
+  if (p.k_new != nullptr)
+    return p.dtype == kF16 ? launch_dt<kF16, true>(p, stream) : launch_dt<kBF16, true>(p, stream);
+  return p.dtype == kF16 ? launch_dt<kF16, false>(p, stream) : launch_dt<kBF16, false>(p, stream);
 }
 
 }  // namespace gqa
