@@ -187,7 +187,10 @@ def graph_time(torch, fn, n_calls, warmup, reps=REPS, out=None):
 
 
 class ColdFlusher:
-    """Reads 1 GiB (evicting the last-level cache) before a single timed launch."""
+    """A single timed launch from cold caches: queued right behind a read of 1 GiB
+    (which evicts the last-level cache and lasts ~150 us, longer than the host
+    takes to enqueue the events and the call), so the events bracket the
+    launch's device time and no host dispatch time."""
 
     def __init__(self, torch, probe):
         self.torch = torch
@@ -196,10 +199,10 @@ class ColdFlusher:
 
     def latency_us(self, fn, i):
         torch = self.torch
-        self.probe.read(self.buf, blocks=2048, unroll=8)
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        self.probe.read(self.buf, blocks=2048, unroll=8)
         a.record(stream)
         fn(i)
         b.record(stream)
