@@ -995,7 +995,8 @@ def main():
     if not args.quick and not only:
         secondary["valu_issue_rates"] = probe.valu_rates()
     roofline = dict(head["roofline"])
-    roofline["kernel"] = "decode_mfma_kernel<128,1> (split merge fused)"
+    roofline["kernel"] = ("decode_mfma_kernel<128,1>" +
+                          (" (split merge fused)" if head["splits"] > 1 else " (one split per (b, g))"))
     line = {
         "metric": METRIC,
         "value": head["GBps"],

@@ -47,17 +47,21 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Split planning.  The decode kernels run one workgroup per (sequence,
-// K/V head, split).  About one workgroup per compute unit (256) is wanted so
-// that every CU streams its share of the cache at once; more splits than
-// that cost more in the merge of the partial results (written, counted and
-// read back once per split) than they gain.  Splits are whole 32-position
-// tiles and at least 128 positions long, which bounds the merge work per
-// position; long caches are cut into slices of at most 3072 positions so that
-// ragged lengths balance across the machine (on the 64-sequence ragged 32k
-// step, 11 splits of 2979 positions measured ~2% faster than 16 of 2048 and
-// than 8, 6 or 4).
-constexpr int64_t kTargetWorkgroups = 256;
-constexpr int64_t kMinSplitLen = 128;
+// K/V head, split) -- per 16 queries of the head when a group has 32 or more
+// (split_units).  A grid of 128 or more work groups runs unsplit: there the
+// merge of the partial results (written, acknowledged, counted and read back)
+// costs more than a wider grid gains (the Llama-7B-sized G=8 step, 128 work
+// groups: 15.41 us unsplit, 15.52 with 2 splits).  Smaller grids are split to
+// about 192 work groups in all (G=4, 64 work groups: 3 splits 11.16 us, 4
+// 11.42, 2 11.71; G=1, 32 work groups: 4 splits 9.6 us, 8 10.4, 3 10.2).
+// Splits are whole 32-position tiles and at least 256 positions long, which
+// bounds the merge work per position; long caches are cut into slices of at
+// most 3072 positions so that ragged lengths balance across the machine (on
+// the 64-sequence ragged 32k step, 11 splits of 2979 positions measured ~2%
+// faster than 16 of 2048 and than 8, 6 or 4).
+constexpr int64_t kUnsplitGrid = 128;
+constexpr int64_t kSplitTarget = 192;
+constexpr int64_t kMinSplitLen = 256;
 constexpr int64_t kMaxSplitLen = 3072;
 
 bool decode_shape_valid(int B, int H, int G, int d, int n_max) {
@@ -67,10 +71,18 @@ bool decode_shape_valid(int B, int H, int G, int d, int n_max) {
   return true;
 }
 
-int plan_splits(int B, int G, int n_max) {
-  if (B <= 0 || n_max <= 0) return 1;
-  const int64_t units = int64_t(B) * G;
-  int64_t s = ceil_div(kTargetWorkgroups, units);
+// Work groups per split: one per (sequence, K/V head), times n_rep / 16 when
+// a group of 32 or more queries runs as work groups of 16 (as decode_impl
+// launches it; GQKVA pairs never do).
+int64_t split_units(int B, int H, int G, bool gqkva) {
+  const int n_rep = gqkva ? H : H / G;
+  const int64_t kv_div = (!gqkva && n_rep > 16 && n_rep % 16 == 0) ? n_rep / 16 : 1;
+  return int64_t(B) * G * kv_div;
+}
+
+int plan_splits(int64_t units, int n_max) {
+  if (units <= 0 || n_max <= 0) return 1;
+  int64_t s = units >= kUnsplitGrid ? 1 : ceil_div(kSplitTarget, units);
   s = std::max<int64_t>(s, ceil_div(n_max, kMaxSplitLen));
   s = std::min<int64_t>(s, std::max<int64_t>(1, ceil_div(n_max, kMinSplitLen)));
   // round the slice length to whole 32-position tiles
@@ -161,7 +173,8 @@ gqa_status decode_impl(const void* q, const void* k, const void* v, const int32_
   if (n_rows64 * d > (int64_t(1) << 40) || int64_t(B) * G * n_max > (int64_t(1) << 40))
     return fail(GQA_ERR_INVALID_ARG, "gqa_decode: problem too large");
 
-  int S_req = num_splits == 0 ? plan_splits(B, G, n_max) : std::min(num_splits, std::max(n_max, 1));
+  int S_req = num_splits == 0 ? plan_splits(split_units(B, H, G, gqkva), n_max)
+                               : std::min(num_splits, std::max(n_max, 1));
   int S, split_len;
   split_geometry(n_max, S_req, &S, &split_len);
   const size_t need = workspace_for(B, Hp, d, S);
@@ -379,13 +392,14 @@ extern "C" {
 int gqa_decode_num_splits(int B, int H, int G, int d, int n_max) {
   if (!decode_shape_valid(B, H, G, d, n_max)) return 0;
   int S, len;
-  split_geometry(n_max, plan_splits(B, G, n_max), &S, &len);
+  split_geometry(n_max, plan_splits(split_units(B, H, G, false), n_max), &S, &len);
   return S;
 }
 
 size_t gqa_decode_workspace_bytes(int B, int H, int G, int d, int n_max, int num_splits) {
   if (!decode_shape_valid(B, H, G, d, n_max) || num_splits < 0) return size_t(-1);
-  int S_req = num_splits == 0 ? plan_splits(B, G, n_max) : std::min(num_splits, std::max(n_max, 1));
+  int S_req = num_splits == 0 ? plan_splits(split_units(B, H, G, false), n_max)
+                               : std::min(num_splits, std::max(n_max, 1));
   int S, len;
   split_geometry(n_max, S_req, &S, &len);
   return workspace_for(B, H, d, S);
@@ -449,7 +463,8 @@ gqa_status gqkva_decode(const void* q, const void* k_cache, const void* v_cache,
 
 size_t gqkva_decode_workspace_bytes(int B, int g_q, int g_kv, int d, int n_max, int num_splits) {
   if (B < 0 || n_max < 0 || d < 1 || num_splits < 0 || g_q < 1 || g_kv < 1) return size_t(-1);
-  int S_req = num_splits == 0 ? plan_splits(B, g_kv, n_max) : std::min(num_splits, std::max(n_max, 1));
+  int S_req = num_splits == 0 ? plan_splits(split_units(B, g_q, g_kv, true), n_max)
+                               : std::min(num_splits, std::max(n_max, 1));
   int S, len;
   split_geometry(n_max, S_req, &S, &len);
   return workspace_for(B, g_q * g_kv, d, S);
@@ -528,7 +543,7 @@ gqa_status gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_
     return decode_impl(q, k_cache, v_cache, seqlens, out, B, H, G, d, n_max, scale, dtype,
                        num_splits, nullptr, 0, stream);
   int S_req = B == 0 ? 1
-                     : (num_splits == 0 ? plan_splits(B, G, n_max)
+                     : (num_splits == 0 ? plan_splits(split_units(B, H, G, false), n_max)
                                         : std::min(num_splits, std::max(n_max, 1)));
   int S, len;
   split_geometry(n_max, S_req, &S, &len);

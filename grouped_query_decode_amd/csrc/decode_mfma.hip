@@ -44,6 +44,8 @@
 #include "device_common.h"
 #include "internal.h"
 
+#include <type_traits>
+
 namespace gqa {
 namespace {
 
@@ -120,10 +122,11 @@ struct UnitPartials {
 };
 
 // Log-sum-exp merge of the ns split partials of head hl (within the group)
-// and 8-column chunk c8 of sequence b, written to out.  Splits are read 8 at
-// a time with all their loads in flight together; the running maximum is
-// rescaled per batch.
-template <int D, int DT>
+// and 8-column chunk c8 of sequence b, written to out.  Splits are read NB at
+// a time (NB = 2, 4 or 8, the smallest batch that holds ns, so no load goes to
+// a slot this call has no split for) with all their loads in flight together;
+// the running maximum is rescaled per batch.
+template <int D, int DT, int NB>
 __device__ __forceinline__ void merge_item(const DecodeProblem& p, const UnitPartials<D>& up, int b, int ns,
                                            int g, int hl, int c8) {
   using H16 = Half16<DT>;
@@ -131,22 +134,22 @@ __device__ __forceinline__ void merge_item(const DecodeProblem& p, const UnitPar
   float M = -INFINITY, L = 0.f;
   f32x4_t Oa = {0.f, 0.f, 0.f, 0.f}, Ob = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-  for (int s0 = 0; s0 < ns; s0 += 8) {
-    u32x2_t ml[8];
-    u32x4_t oa[8], ob[8];
+  for (int s0 = 0; s0 < ns; s0 += NB) {
+    u32x2_t ml[NB];
+    u32x4_t oa[NB], ob[NB];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < NB; ++u) {
       const int pr = hl * S + s0 + u;
       ml[u] = __builtin_amdgcn_raw_buffer_load_b64(up.ml, pr * 8, 0, kDeviceCoherent);
       oa[u] = __builtin_amdgcn_raw_buffer_load_b128(up.o, pr * (D * 4) + c8 * 32, 0, kDeviceCoherent);
       ob[u] = __builtin_amdgcn_raw_buffer_load_b128(up.o, pr * (D * 4) + c8 * 32 + 16, 0, kDeviceCoherent);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < NB; ++u)
       if (s0 + u >= ns) ml[u][1] = 0u;             // not a split of this call: skipped
     float cm = M;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < NB; ++u)
       if (__uint_as_float(ml[u][1]) > 0.f) cm = fmaxf(cm, __uint_as_float(ml[u][0]));
     if (cm == -INFINITY) continue;               // nothing seen yet
     const float f0 = __builtin_amdgcn_exp2f(M - cm);   // 0 while M is -inf
@@ -154,7 +157,7 @@ __device__ __forceinline__ void merge_item(const DecodeProblem& p, const UnitPar
     Oa *= f0;
     Ob *= f0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < NB; ++u) {
       const float lu = __uint_as_float(ml[u][1]);
       // Slots of splits that did not run in this call (or saw nothing) hold
       // stale bytes -- possibly inf or NaN -- so they are selected away, never
@@ -540,9 +543,14 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   if (threadIdx.x == 0)            // ready for the next call (nothing reads it in this one)
     __hip_atomic_store(p.counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   constexpr int kC8 = D / 8;
+  auto merge_all = [&](auto NB) {
 #pragma unroll 1
-  for (int t = threadIdx.x; t < p.n_rep * kC8; t += blockDim.x)
-    merge_item<D, DT>(p, up, b, ns, g, t / kC8, t % kC8);
+    for (int t = threadIdx.x; t < p.n_rep * kC8; t += blockDim.x)
+      merge_item<D, DT, decltype(NB)::value>(p, up, b, ns, g, t / kC8, t % kC8);
+  };
+  if (ns <= 2) merge_all(std::integral_constant<int, 2>{});
+  else if (ns <= 4) merge_all(std::integral_constant<int, 4>{});
+  else merge_all(std::integral_constant<int, 8>{});
 #ifdef GQA_DECODE_TIMELINE
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();

@@ -122,11 +122,14 @@ def test_decode_empty_batch_is_a_noop(lib):
 
 
 def test_decode_workspace_checked_before_launch(lib):
-    need = lib.gqa_decode_workspace_bytes(16, 32, 8, 128, 1024, 0)
+    # 4 sequences x 8 K/V heads: 32 work groups, planned as 4 splits
+    need = lib.gqa_decode_workspace_bytes(4, 32, 8, 128, 1024, 0)
     assert need > 0
-    assert _decode(lib, B=16, H=32, G=8, d=128, n=1024) == WORKSPACE
-    assert _decode(lib, B=16, H=32, G=8, d=128, n=1024, ws=P, ws_bytes=need - 1) == WORKSPACE
-    assert _decode(lib, B=16, H=32, G=8, d=128, n=1024, ws=P_MIS, ws_bytes=need) == WORKSPACE
+    assert _decode(lib, B=4, H=32, G=8, d=128, n=1024) == WORKSPACE
+    assert _decode(lib, B=4, H=32, G=8, d=128, n=1024, ws=P, ws_bytes=need - 1) == WORKSPACE
+    assert _decode(lib, B=4, H=32, G=8, d=128, n=1024, ws=P_MIS, ws_bytes=need) == WORKSPACE
+    # forced splits need one whatever the planner would choose
+    assert _decode(lib, B=16, H=32, G=8, d=128, n=1024, splits=2) == WORKSPACE
 
 
 def test_split_planner_is_host_only_and_consistent(lib):
@@ -144,10 +147,11 @@ def test_split_planner_is_host_only_and_consistent(lib):
         assert ws == lib.gqa_decode_workspace_bytes(B, H, G, d, n, S)
     # long ragged caches are cut into bounded slices
     assert lib.gqa_decode_num_splits(64, 32, 8, 128, 32768) >= 11
-    # about one workgroup per compute unit, splits of at least 128 positions
-    planned = {(16, 32, 32, 128, 1024): 1, (16, 32, 8, 128, 1024): 2, (16, 32, 4, 128, 1024): 4,
-               (16, 32, 1, 128, 1024): 8, (32, 64, 8, 64, 2048): 1, (1, 8, 2, 64, 128): 1,
-               (64, 32, 8, 128, 32768): 11}
+    # unsplit from 128 work groups per split, else about 192 in all; splits of
+    # 256 .. 3072 positions (32 queries per K/V head count as two work groups)
+    planned = {(16, 32, 32, 128, 1024): 1, (16, 32, 8, 128, 1024): 1, (16, 32, 4, 128, 1024): 3,
+               (16, 32, 1, 128, 1024): 4, (32, 64, 8, 64, 2048): 1, (1, 8, 2, 64, 128): 1,
+               (64, 32, 8, 128, 32768): 11, (8, 32, 8, 128, 1024): 3, (4, 32, 8, 128, 4096): 6}
     for shape, S in planned.items():
         assert lib.gqa_decode_num_splits(*shape) == S, shape
     # forced split counts
@@ -240,7 +244,7 @@ def test_decode_append_rejects_bad_arguments(lib):
     assert "aligned" in lib.gqa_last_error().decode()
     assert _append(lib, H=6, G=4) == INVALID
     assert _append(lib, d=96) == UNSUPPORTED
-    assert _append(lib, B=16, H=32, G=8, d=128, n=1024) == WORKSPACE
+    assert _append(lib, B=4, H=32, G=8, d=128, n=1024) == WORKSPACE
     # B = 0: nothing to do, no pointer looked at
     assert _append(lib, q=z, kn=z, vn=z, k=z, v=z, sl=z, out=z, B=0) == OK
 
@@ -274,10 +278,12 @@ def test_gqkva_arguments_and_workspace(lib):
     assert dec(d=96) == UNSUPPORTED
     assert dec(q=z, k=z, v=z, sl=z, out=z, B=0) == OK
     # a ratio that is not a whole number is fine for GQKVA: only the workspace is missing here
-    assert dec(B=16, gq=3, gkv=8, d=128, n=1024) == WORKSPACE
-    need = lib.gqkva_decode_workspace_bytes(16, 3, 8, 128, 1024, 0)
-    S = lib.gqa_decode_num_splits(16, 8, 8, 128, 1024)          # same plan as G = 8 K/V heads
-    assert need == 65536 + (16 * 24 * S * 128 * 4 + 255) // 256 * 256 + 16 * 24 * S * 2 * 4
+    assert dec(B=4, gq=3, gkv=8, d=128, n=1024) == WORKSPACE
+    need = lib.gqkva_decode_workspace_bytes(4, 3, 8, 128, 1024, 0)
+    S = lib.gqa_decode_num_splits(4, 8, 8, 128, 1024)           # same plan as G = 8 K/V heads
+    assert S > 1
+    assert need == 65536 + (4 * 24 * S * 128 * 4 + 255) // 256 * 256 + 4 * 24 * S * 2 * 4
+    assert lib.gqkva_decode_workspace_bytes(16, 3, 8, 128, 1024, 0) == 0   # 128 work groups: unsplit
     assert lib.gqkva_decode_workspace_bytes(16, 3, 0, 128, 1024, 0) == ctypes.c_size_t(-1).value
     assert lib.gqkva_prefill_causal(z, z, z, z, 0, 16, 2, 3, 64, 0.1, BF16, None) == OK
     assert lib.gqkva_prefill_causal(P, P, P, P, 1, 16, 2, 0, 64, 0.1, BF16, None) == INVALID

@@ -47,11 +47,12 @@ def _pair(x, scale, num_splits):
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_noalloc_matches_workspace_decode_two_calls(dt):
     dtype = {"bf16": torch.bfloat16, "f32": torch.float32}[dt]
-    # first call: Llama-7B-sized layer (planner's split count), second: a
-    # smaller ragged batch with NaN beyond the lengths and more forced splits
-    # than the first call had (slots the first call left are stale)
+    # first call: Llama-7B-sized layer with 3 forced splits (the planner runs
+    # this shape unsplit), second: a smaller ragged batch with NaN beyond the
+    # lengths and more forced splits than the first call had (slots the first
+    # call left are stale)
     cases = [
-        dict(B=16, H=32, G=8, d=128, N=1024, seqlens="uniform", splits=0, seed=40),
+        dict(B=16, H=32, G=8, d=128, N=1024, seqlens="uniform", splits=3, seed=40),
         dict(B=3, H=8, G=2, d=64, N=700, seqlens=[700, 1, 333], splits=7, seed=41),
     ]
     for i, c in enumerate(cases):
