@@ -255,12 +255,12 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   // Append (when k_new is given): the new token's k, v belong in slot
   // raw_len-1 if that slot exists.  The split holding that slot writes them
   // to the cache (the first work group of the K/V head, when several share
-  // it) and into an LDS copy (lanes of wave 0), from which wave 0 attends them
-  // before its first cached tile (no workgroup reads that slot from the cache
-  // in this launch); its stream of cached rows stops just before the slot.
+  // it) and into an LDS copy, which becomes the slot's row of its tile (no
+  // workgroup reads that slot from the cache in this launch: the split's
+  // loads end just before it).
   __shared__ __attribute__((aligned(16))) char s_new[2 * D * 2];
   const int p_new = (APPEND && raw_len >= 1 && raw_len <= p.n_max) ? raw_len - 1 : -1;
-  const bool owner = p_new >= j0 && p_new < j1;
+  const bool owner = APPEND && p_new >= j0 && p_new < j1;
   if (owner && threadIdx.x < 2 * C::kChunks) {
     const int c = threadIdx.x % C::kChunks;
     const bool is_v = threadIdx.x >= C::kChunks;
@@ -302,6 +302,10 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   // the end return zeros without touching memory, so the loads need no
   // branches and the tile pipeline below has a fixed shape.
   const int nvalid = owner ? p_new - j0 : (j1 > j0 ? j1 - j0 : 0);
+  // positions this split attends: the cached ones, plus the appended token
+  const int rel_new = owner ? p_new - j0 : -1;
+  const int tile_new = owner ? rel_new / kKT : -1;
+  const int nattend = owner ? rel_new + 1 : nvalid;
   const uint32_t vbytes = uint32_t(nvalid) * uint32_t(D * 2);
   const __amdgpu_buffer_rsrc_t rk = rsrc(kb + int64_t(j0) * D, vbytes);
   const __amdgpu_buffer_rsrc_t rv = rsrc(vb + int64_t(j0) * D, vbytes);
@@ -341,6 +345,17 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
       const int r = idx / C::kChunks, c = idx % C::kChunks;
       *reinterpret_cast<u32x4_t*>(myk + r * (D * 2) + ((c ^ kswz<D>(r)) << 4)) = kr[t];
       *reinterpret_cast<u32x4_t*>(myv + r * C::kPitch + c * 16) = vr[t];
+    }
+    // the appended token is row rel_new of its tile: its cache row was not
+    // loaded (the loads end before it), so its k, v come from the LDS copy
+    if constexpr (APPEND) {
+      if (tile == tile_new && lane < C::kChunks) {
+        const int r = rel_new % kKT;
+        *reinterpret_cast<u32x4_t*>(myk + r * (D * 2) + ((lane ^ kswz<D>(r)) << 4)) =
+            *reinterpret_cast<const u32x4_t*>(s_new + lane * 16);
+        *reinterpret_cast<u32x4_t*>(myv + r * C::kPitch + lane * 16) =
+            *reinterpret_cast<const u32x4_t*>(s_new + D * 2 + lane * 16);
+      }
     }
     // this tile's registers are free: fetch the wave's next tile into them
     if (prefetch) load_tile(tile + nw, kr, vr);
@@ -416,36 +431,19 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
 
   // Wave w takes tiles w, w + nw, w + 2 nw, ...; each tile's processing
   // issues the loads of the next one into the registers it has just freed.
-  const int ntiles = (nvalid + kKT - 1) / kKT;
+  const int ntiles = (nattend + kKT - 1) / kKT;
+  // the LDS copy of k_new, v_new is read by whichever wave has the slot's
+  // tile (meeting here, before the tile loads go out, measured faster than
+  // after them)
+  if constexpr (APPEND) {
+    if (owner) __syncthreads();
+  }
   KTile ka;
   VTile va;
   int tile = wave;
   load_tile(tile, ka, va);
-  if constexpr (APPEND) {
-    // The appended token first, as a one-row tile on wave 0 (its k, v from
-    // the LDS copy this wave wrote above), while the wave's first cached tile
-    // is still in flight: it then costs nothing on the path after the last
-    // tile.  (Attending it first instead of last changes only the rounding
-    // order of the online softmax.)
-    if (owner && wave == 0) {
-      lds_wave_sync();
-      KTile kn;
-      VTile vn;
-#pragma unroll
-      for (int t = 0; t < C::kTileLoads; ++t) {
-        u32x4_t wk = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
-        if (t == 0 && lane < C::kChunks) {
-          wk = *reinterpret_cast<const u32x4_t*>(s_new + lane * 16);
-          wv = *reinterpret_cast<const u32x4_t*>(s_new + D * 2 + lane * 16);
-        }
-        kn[t] = wk;
-        vn[t] = wv;
-      }
-      process(0, kn, vn, 1, false);
-    }
-  }
   for (; tile < ntiles; tile += nw) {
-    process(tile, ka, va, nvalid, true);
+    process(tile, ka, va, nattend, true);
     if (tile == wave) GQA_PHASE(2);
   }
   GQA_PHASE(3);
