@@ -589,6 +589,17 @@ def bench_meanpool_batch(torch, gqa, synth, count, warmup, reps, means, key):
     return res
 
 
+class _Progress(dict):
+    """The secondary results; each workload's time goes to stderr as it finishes (a progress line)."""
+
+    def __setitem__(self, key, value):
+        super().__setitem__(key, value)
+        if isinstance(value, dict):
+            t = value.get("ms_per_call")
+            msg = f"{t * 1e3:.2f} us per call" if t is not None else "done"
+            print(f"[bench] {key}: {msg}", file=sys.stderr, flush=True)
+
+
 def g_sweep_fit(points):
     """Least-squares line time = fixed + bytes / bandwidth over the G sweep."""
     xs = [p["bytes_per_call"] for p in points]
@@ -907,7 +918,8 @@ def main():
                            HEADLINE_KEY, keep_sample=want_cpu)
     if s:
         samples.append(s)
-    secondary = {}
+    print(f"[bench] {HEADLINE_KEY}: {head['ms_per_call'] * 1e3:.2f} us per call", file=sys.stderr, flush=True)
+    secondary = _Progress()
     sweep = [head]
     for g in (32, 4, 1):
         k = f"llama7b_decode_G{g}"
