@@ -51,9 +51,10 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // (split_units).  A grid of 128 or more work groups runs unsplit: there the
 // merge of the partial results (written, acknowledged, counted and read back)
 // costs more than a wider grid gains (the Llama-7B-sized G=8 step, 128 work
-// groups: 15.41 us unsplit, 15.52 with 2 splits).  Smaller grids are split to
-// about 192 work groups in all (G=4, 64 work groups: 3 splits 11.16 us, 4
-// 11.42, 2 11.71; G=1, 32 work groups: 4 splits 9.6 us, 8 10.4, 3 10.2).
+// groups: 14.7 us unsplit, 15.1 with 2 splits, 16.6 with 3).  Smaller grids
+// are split to about 192 work groups in all (G=4, 64 work groups: 3 splits
+// 10.7 us, 4 11.0, 2 11.2, 6 12.3; G=1, 32 work groups: 4 splits 9.0 us, 3
+// 9.5, 6 9.6, 8 9.8, 2 10.4).
 // Splits are whole 32-position tiles and at least 256 positions long, which
 // bounds the merge work per position; long caches are cut into slices of at
 // most 3072 positions so that ragged lengths balance across the machine (on

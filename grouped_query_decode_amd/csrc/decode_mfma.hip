@@ -314,20 +314,32 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
   // LDS area: K in the score MFMA's A layout, V for the transposing reads.
   const int row_lane = lane * 16;
   // Both streams carry the non-temporal hint (each row is read once per work
-  // group; K with it measured 5-7% faster at every decode shape).
+  // group; K with it measured 5-7% faster at every decode shape).  At d = 128
+  // the next tile's K loads are issued as soon as this tile's K rows are in
+  // LDS and its V loads once V is (1-2% faster at d = 128 than issuing both
+  // after V; 2.6% slower at d = 64, which keeps the single issue point).
+  constexpr bool kSplitPrefetch = D == 128;
   typedef u32x4_t KTile[C::kTileLoads];
   typedef u32x4_t VTile[C::kTileLoads];
-  auto load_tile = [&](int tile, KTile& kr, VTile& vr) {
+  // (each group of loads is kept together and in program order, so that the
+  // wait before a tile's use covers just the loads issued before it)
+  auto load_k = [&](int tile, KTile& kr) {
     const int base = tile * (kKT * D * 2);
 #pragma unroll
     for (int t = 0; t < C::kTileLoads; ++t)
       kr[t] = __builtin_amdgcn_raw_buffer_load_b128(rk, base + row_lane + t * 1024, 0, kNonTemporal);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto load_v = [&](int tile, VTile& vr) {
+    const int base = tile * (kKT * D * 2);
 #pragma unroll
     for (int t = 0; t < C::kTileLoads; ++t)
       vr[t] = __builtin_amdgcn_raw_buffer_load_b128(rv, base + row_lane + t * 1024, 0, kNonTemporal);
-    // keep each tile's loads together and in program order, so that the
-    // wait before a tile's use covers just the loads issued before it
     __builtin_amdgcn_sched_barrier(0);
+  };
+  auto load_tile = [&](int tile, KTile& kr, VTile& vr) {
+    load_k(tile, kr);
+    load_v(tile, vr);
   };
 
   // V^T operand of the output MFMA by transposing LDS reads: within each
@@ -346,7 +358,17 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
       const int idx = t * 64 + lane;
       const int r = idx / C::kChunks, c = idx % C::kChunks;
       *reinterpret_cast<u32x4_t*>(myk + r * (D * 2) + ((c ^ kswz<D>(r)) << 4)) = kr[t];
-      *reinterpret_cast<u32x4_t*>(myv + r * C::kPitch + c * 16) = vr[t];
+      if constexpr (!kSplitPrefetch) *reinterpret_cast<u32x4_t*>(myv + r * C::kPitch + c * 16) = vr[t];
+    }
+    if constexpr (kSplitPrefetch) {
+      // K is in LDS: the next tile's K loads go out while this tile's V lands
+      if (prefetch) load_k(tile + nw, kr);
+#pragma unroll
+      for (int t = 0; t < C::kTileLoads; ++t) {
+        const int idx = t * 64 + lane;
+        const int r = idx / C::kChunks, c = idx % C::kChunks;
+        *reinterpret_cast<u32x4_t*>(myv + r * C::kPitch + c * 16) = vr[t];
+      }
     }
     // the appended token is row rel_new of its tile: its cache row was not
     // loaded (the loads end before it), so its k, v come from the LDS copy
@@ -360,7 +382,10 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
       }
     }
     // this tile's registers are free: fetch the wave's next tile into them
-    if (prefetch) load_tile(tile + nw, kr, vr);
+    if (prefetch) {
+      if constexpr (kSplitPrefetch) load_v(tile + nw, vr);
+      else load_tile(tile + nw, kr, vr);
+    }
     lds_wave_sync();
     // scores: A = K rows 16*blk + lo, chunk 4*ks + hi, from LDS
     u32x4_t kop[2][C::kSteps];
@@ -558,6 +583,15 @@ __global__ __launch_bounds__(256, NHB == 1 ? 2 : 1) void decode_mfma_kernel(Deco
 #endif
 }
 
+// Static LDS of the decode kernel (tiles and merge area, the appended row,
+// the merge flag), and the per-workgroup total above which only one
+// workgroup fits in a compute unit's 160 KB.
+template <int D>
+constexpr size_t kDecodeStaticLds = size_t(Cfg<D>::kLds) + 2 * D * 2 + 16;
+constexpr size_t kOnePerCuLds = 82 * 1024;
+constexpr int64_t kOnePerCuGrid = 1024;
+static_assert(kDecodeStaticLds<128> < kOnePerCuLds, "padding");
+
 template <int D, int NHB, int DT, bool APPEND>
 hipError_t launch_t(const DecodeProblem& p, hipStream_t stream) {
   const int64_t blocks = int64_t(p.B) * (p.G / p.kv_div) * p.num_splits;
@@ -566,8 +600,16 @@ hipError_t launch_t(const DecodeProblem& p, hipStream_t stream) {
   // one wave per 32-position tile of a split, at most four
   const int tiles = (p.split_len + kKT - 1) / kKT;
   const int waves = tiles >= 4 ? 4 : (tiles >= 2 ? 2 : 1);
+  // A grid of several rounds of workgroups at d = 128 runs one workgroup per
+  // compute unit (unused dynamic LDS makes a second one not fit): two resident
+  // workgroups keep 128 KB of tiles in flight per compute unit, past the point
+  // where more requests only lengthen each one's round trip (the ragged 32k
+  // step: 774-777 us against 802).  Grids of one or two rounds keep two per
+  // compute unit (a 384-workgroup grid would take two rounds instead of one).
+  const int64_t wgs = blocks * p.kv_div;
+  const size_t lds_pad = (D == 128 && wgs >= kOnePerCuGrid) ? kOnePerCuLds - kDecodeStaticLds<D> : 0;
   hipLaunchKernelGGL((decode_mfma_kernel<D, NHB, DT, APPEND>), dim3(unsigned(blocks), unsigned(p.kv_div)),
-                     dim3(64 * waves), 0, stream, p);
+                     dim3(64 * waves), lds_pad, stream, p);
   return hipGetLastError();
 }
 
