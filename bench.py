@@ -13,14 +13,21 @@ the 256 MB last-level cache cannot serve a call from an earlier one.
 Timing: K calls are captured into one HIP graph (the library launches on the
 capturing stream) and the graph is replayed R times (default 7), each replay
 bracketed by a device synchronisation and timed with HIP events on the launch
-stream; the per-call time of a replay is its elapsed time / K, and the line
+stream, queued behind a ~150 us read of 1 GiB so that the host's graph launch
+overlaps it and the events bracket exactly the K calls; the per-call time of a replay is its elapsed time / K, and the line
 reports the median (``ms_per_step``) and the minimum.  Graph replay keeps the
 host's per-call dispatch cost (Python, ctypes, argument checks) out of the
 measurement, so the figure is the GPU's: kernel time plus the gap between
 back-to-back kernels.  After timing, the graph's output is compared bit for
 bit with an eager call of the same step.  The headline is timed with exactly
 K = --steps calls per replay; every other workload with enough calls for a
-replay of >= 50 ms (and >= 200 calls).
+replay of >= 50 ms (and >= 200 calls).  Every plain decode is also timed a
+second way, as K back-to-back calls of the C entry point made directly from
+C behind the same 1 GiB read (``direct_call_loop_ms_per_call``, median of R
+runs).  A graph replay carries a fixed ~10 us of device-side cost, so a
+headline of fewer than 200 steps reports the direct calls instead (at 20
+steps: 14.6 us per step against 14.8 by graph replay; at 4000: 14.5 against
+14.3, the kernel trace's 14.3).
 
 Also reported, each with its own roofline block (``secondary``): the G sweep
 {32, 8, 4, 1} on the same queries with a linear fit of time against bytes
@@ -147,13 +154,23 @@ def calls_for(ms_per_call, min_rep_ms=None):
     return int(min(MAX_CALLS, max(MIN_CALLS, math.ceil(rep_ms / max(ms_per_call, 1e-6)))))
 
 
+# Device work queued ahead of each timed replay (set once the cache-evicting
+# read exists): a ~150 us read of 1 GiB, during which the host submits the
+# graph, so the start event is taken when the first timed kernel can start
+# and a replay of a few calls does not carry the graph launch's host latency
+# (~9 us: 20 calls of the headline step read 14.8 us per call without it,
+# 14.3 with it and with 4000 calls).
+LEAD = None
+
+
 def graph_time(torch, fn, n_calls, warmup, reps=REPS, out=None):
     """Per-call milliseconds of fn(0) .. fn(n_calls-1) captured into one HIP graph.
 
     ``warmup`` eager calls first; then one untimed replay and ``reps`` timed
     replays, each bracketed by torch.cuda.synchronize() and timed with events
-    on the launch stream.  With ``out`` (the tensor the calls write), the graph
-    result is compared bit for bit with an eager repeat of the last call.
+    on the launch stream (behind LEAD's read, when set, so that the events
+    bracket exactly the calls).  With ``out`` (the tensor the calls write), the
+    graph result is compared bit for bit with an eager repeat of the last call.
     """
     for i in range(warmup):
         fn(i)
@@ -169,6 +186,8 @@ def graph_time(torch, fn, n_calls, warmup, reps=REPS, out=None):
     for _ in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        if LEAD is not None:
+            LEAD()
         a.record(stream)
         graph.replay()
         b.record(stream)
@@ -196,6 +215,10 @@ class ColdFlusher:
         self.torch = torch
         self.probe = probe
         self.buf = torch.ones(1 << 30, dtype=torch.uint8, device=DEV)
+
+    def lead(self):
+        """Enqueue the 1 GiB read (no host wait): device work ahead of a timed region."""
+        self.probe.read(self.buf, blocks=2048, unroll=8)
 
     def latency_us(self, fn, i):
         torch = self.torch
@@ -278,6 +301,35 @@ class ReadProbe:
             res[name] = {"ns_per_wave_instruction_per_cu": round(ms * 1e6 / wi, 4),
                          "bytes_per_ns_per_cu": round(64 * lane_bytes * wi / (ms * 1e6), 1)}
         return res
+
+    def decode_call_loop(self, gqa, xs, out, ws, B, H, G, d, N, scale, n_calls, warmup=20, reps=3,
+                         lead=None):
+        """Per-call ms of n_calls back-to-back gqa_decode_split calls made directly from C
+        (gqa_probe_time_decode_calls; no Python, no graph), rotating over the input sets
+        xs, ``reps`` runs -- each queued behind a read of ``lead`` (a device buffer) when
+        given.  Returns the per-run figures."""
+        vp, i32 = ctypes.c_void_p, ctypes.c_int
+        f = self.lib.gqa_probe_time_decode_calls
+        f.argtypes = ([vp] * 5 + [i32, vp] + [i32] * 5 + [ctypes.c_float] + [i32] * 2 +
+                      [vp, ctypes.c_size_t, i32, i32, vp, ctypes.c_size_t, vp, vp, vp])
+        f.restype = i32
+        lead_ptr = vp(0) if lead is None else vp(lead.data_ptr())
+        lead_bytes = 0 if lead is None else lead.numel() * lead.element_size()
+        R = len(xs)
+        arr = lambda key: (vp * R)(*[x[key].data_ptr() for x in xs])  # noqa: E731
+        q, k, v, sl = arr("q"), arr("k_cache"), arr("v_cache"), arr("seqlens")
+        fn = ctypes.cast(gqa.load_library().gqa_decode_split, vp)
+        stream = vp(self.torch.cuda.current_stream().cuda_stream)
+        runs = []
+        for _ in range(reps):
+            ms = ctypes.c_float(0.0)
+            rc = f(fn, q, k, v, sl, R, vp(out.data_ptr()), B, H, G, d, N, scale, gqa.DTYPE_CODES[out.dtype], 0,
+                   vp(ws.data_ptr()), ws.numel() * ws.element_size(), warmup, n_calls, lead_ptr, lead_bytes,
+                   vp(self.sink.data_ptr()), stream, ctypes.byref(ms))
+            if rc != 0:
+                raise RuntimeError(f"gqa_probe_time_decode_calls failed ({rc})")
+            runs.append(ms.value / n_calls)
+        return runs
 
     def read(self, buf, blocks, unroll):
         rc = self.lib.gqa_probe_hbm_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
@@ -363,7 +415,7 @@ def _finish_timing(res, t):
 
 
 def bench_decode(torch, gqa, synth, name, G, n_calls, warmup, reps, flusher, means, key,
-                 append=False, dtype=None, keep_sample=False):
+                 append=False, dtype=None, keep_sample=False, direct_timing=False):
     w = synth.WORKLOADS[name]
     B, H, d, N = w.B, w.H, w.d, w.N
     dt = dtype or w.dtype
@@ -391,6 +443,15 @@ def bench_decode(torch, gqa, synth, name, G, n_calls, warmup, reps, flusher, mea
     if n_calls is None:
         n_calls = calls_for(_eager_ms(torch, call, 20))
     t = graph_time(torch, call, n_calls, warmup, reps=reps, out=out)
+    graph_ms = t["median_ms"]
+    direct = None
+    if not append:
+        runs = flusher.probe.decode_call_loop(gqa, reps_in, out, ws, B, H, G, d, N, scale, n_calls,
+                                              warmup=max(warmup, 1), reps=reps, lead=flusher.buf)
+        direct = statistics.median(runs)
+        if direct_timing:
+            # the K steps timed as K direct calls queued behind the lead read
+            t = dict(t, median_ms=direct, min_ms=min(runs), rep_ms=[round(x, 6) for x in runs])
     cold = flusher.latency_us(call, 0)
     total_pos = int(torch.clamp(reps_in[0]["seqlens"].long(), 0, N).sum().item())
     for r in reps_in[1:]:
@@ -410,6 +471,8 @@ def bench_decode(torch, gqa, synth, name, G, n_calls, warmup, reps, flusher, mea
         "tokens_per_s": round(B / (ms * 1e-3), 1),
         "TFLOPs": round(decode_flops(H, total_pos, d) / (ms * 1e-3) / 1e12, 2),
         "cold_latency_us": cold,
+        "direct_call_loop_ms_per_call": None if direct is None else round(direct, 6),
+        "graph_replay_ms_per_call": round(graph_ms, 6),
         "roofline": _roofline_hbm(gbps, "decode_mfma_kernel" if dt != "f32" else "rows_valu_kernel",
                                   nbytes, key, means),
     })
@@ -905,6 +968,8 @@ def main():
               flush=True)
         return
     flusher = ColdFlusher(torch, probe)
+    global LEAD
+    LEAD = flusher.lead
     means = stored_kernel_means()
     TRAFFIC.update(stored_traffic())
     want_cpu = not args.no_cpu_baseline
@@ -914,8 +979,12 @@ def main():
     reps = args.reps
 
     name, G = HEADLINE
+    # K steps are timed as a graph replay when K >= MIN_CALLS (the replay's fixed
+    # ~10 us of device-side cost is then amortised), else as K direct calls from
+    # C queued behind the lead read (no per-replay cost, ~0.1 us more per call)
+    direct_headline = args.steps < MIN_CALLS
     head, s = bench_decode(torch, gqa, synth, name, G, args.steps, args.warmup, reps, flusher, means,
-                           HEADLINE_KEY, keep_sample=want_cpu)
+                           HEADLINE_KEY, keep_sample=want_cpu, direct_timing=direct_headline)
     if s:
         samples.append(s)
     print(f"[bench] {HEADLINE_KEY}: {head['ms_per_call'] * 1e3:.2f} us per call", file=sys.stderr, flush=True)
@@ -1024,9 +1093,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "B": head["B"], "H": head["H"], "G": G, "d": head["d"],
                    "N": head["N"], "splits": head["splits"], "replicas": head["replicas"]},
-        "timing": {"method": "HIP graph of `steps` calls, replayed `reps` times; median per call",
+        "timing": {"method": ("`steps` back-to-back calls of the C entry point made directly from C, "
+                              "queued behind a 1 GiB device read (so the events bracket exactly the calls), "
+                              "`reps` runs; median per call") if direct_headline else
+                             ("HIP graph of `steps` calls, replayed `reps` times behind a 1 GiB device read; "
+                              "median per call"),
                    "reps": reps, "ms_per_step_min": head["ms_per_call_min"],
                    "rep_ms_per_step": head["rep_ms_per_call"],
+                   "graph_replay_ms_per_step": head["graph_replay_ms_per_call"],
+                   "direct_call_loop_ms_per_step": head["direct_call_loop_ms_per_call"],
                    "graph_matches_eager": head["graph_matches_eager"],
                    "cold_latency_us": head["cold_latency_us"]},
         "tokens_per_s": head["tokens_per_s"],

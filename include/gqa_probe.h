@@ -56,6 +56,32 @@ int gqa_probe_valu_rate(float* out, int kind, int blocks, void* stream);
  */
 int gqa_probe_lds_rate(uint32_t* sink, int kind, int blocks, void* stream);
 
+/*
+ * gqa_probe_time_decode_calls - timing of the decode step by direct calls:
+ * `warmup` untimed calls, then `calls` back-to-back calls of `fn` -- a
+ * pointer to libgqa.so's gqa_decode_split, passed in so that this library
+ * does not link the attention library -- made directly from C, call i
+ * reading input set i % n_inputs, between two HIP events recorded on
+ * `stream`.  With lead_buf, a read of lead_bytes of it (gqa_probe_hbm_read,
+ * 2048 blocks, unroll 8; sink as there) is queued just before the start
+ * event: the host enqueues the calls while it runs, so the events bracket
+ * exactly the calls.  The elapsed milliseconds of the timed calls go to *ms.
+ *
+ *   q, k_cache, v_cache, seqlens  host arrays of n_inputs device pointers
+ *   other arguments               passed through to gqa_decode_split
+ * Returns 0; 1 for an invalid argument (nothing called; an invalid lead read
+ * after the warmup calls also returns 1); 2 if a call returned a non-zero
+ * status (its detail: gqa_last_error in libgqa.so); 4 for a failed HIP
+ * event or synchronisation call.
+ */
+int gqa_probe_time_decode_calls(void* fn, const void* const* q, const void* const* k_cache,
+                                const void* const* v_cache, const int32_t* const* seqlens,
+                                int n_inputs, void* out, int B, int H, int G, int d, int n_max,
+                                float scale, int dtype, int num_splits, void* workspace,
+                                size_t workspace_bytes, int warmup, int calls,
+                                const void* lead_buf, size_t lead_bytes, uint32_t* sink,
+                                void* stream, float* ms);
+
 #ifdef __cplusplus
 }
 #endif

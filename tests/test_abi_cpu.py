@@ -55,7 +55,8 @@ def test_probe_library_exports_its_header():
         pytest.fail("libgqa_probe.so is not built: run __graft_entry__.build() first")
     raw = ctypes.CDLL(path)
     names = declared_functions(os.path.join(ROOT, "include", "gqa_probe.h"))
-    assert names == ["gqa_probe_hbm_read", "gqa_probe_lds_rate", "gqa_probe_valu_rate"]
+    assert names == ["gqa_probe_hbm_read", "gqa_probe_lds_rate", "gqa_probe_time_decode_calls",
+                     "gqa_probe_valu_rate"]
     for name in names:
         assert hasattr(raw, name)
     f = raw.gqa_probe_hbm_read
@@ -80,6 +81,24 @@ def test_probe_library_exports_its_header():
     assert lr(P, 2, 512, None) == 1                       # kind
     assert lr(ctypes.c_void_p(0), 0, 512, None) == 1
     assert lr(P, 1, 0, None) == 1
+    t = raw.gqa_probe_time_decode_calls
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    t.argtypes = ([vp] * 5 + [i32, vp] + [i32] * 5 + [ctypes.c_float] + [i32] * 2 +
+                  [vp, ctypes.c_size_t, i32, i32, vp, ctypes.c_size_t, vp, vp, vp])
+    t.restype = i32
+    arr = (vp * 1)(P.value)
+    ms = ctypes.c_float(0.0)
+    fn = ctypes.cast(ctypes.CDLL(gqa.library_path()).gqa_decode_split, vp)
+    args = lambda f, n_in, calls, H, G, lead=None: (f, arr, arr, arr, arr, n_in, P, 1, H, G, 128,  # noqa: E731
+                                                    16, 0.1, 1, 0, None, 0, 1, calls, lead, 1 << 20,
+                                                    None, None, ctypes.byref(ms))
+    assert t(*args(vp(0), 1, 10, 8, 2)) == 1              # no entry point
+    assert t(*args(fn, 0, 10, 8, 2)) == 1                 # no inputs
+    assert t(*args(fn, 1, 0, 8, 2)) == 1                  # no calls
+    assert t(*args(fn, 1, 10, 8, 2, lead=P)) == 1         # a lead read without a sink
+    # a call the library refuses on the host (H not a multiple of G) stops the
+    # loop with status 2 before any GPU work
+    assert t(*args(fn, 1, 10, 8, 3)) == 2
 
 
 def test_status_strings(lib):

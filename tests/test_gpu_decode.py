@@ -279,6 +279,45 @@ def test_t5xxl_cross_attention_decode():
     assert_close(_run(x, scale), _oracle(x, scale), torch.bfloat16, "t5xxl")
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_grid_of_many_workgroup_rounds(dt, num_splits):
+    """A d = 128 grid of 1024 or more workgroups (128 sequences x 8 K/V heads;
+    with 3 splits 3072), which the library launches one workgroup per compute
+    unit: ragged lengths with NaN beyond them, every output row against the
+    oracle."""
+    B, H, G, d, n_max = 128, 32, 8, 128, 520
+    announce(f"decode {B}x{H}/{G} d={d} N={n_max} {dt} splits={num_splits}")
+    x = synth.decode_inputs(B, H, G, d, n_max, dtype=dt, seed=31, device=DEV, seqlens="uniform",
+                            nan_tail=True)
+    scale = synth.scale_for(d)
+    out = _run(x, scale, num_splits=num_splits)
+    assert_close(out, _oracle(x, scale), synth.torch_dtype(dt), f"{B}x{G} grid, {dt}, S={num_splits}")
+
+
+def test_append_grid_of_many_workgroup_rounds():
+    """The fused append on the same 1024-workgroup d = 128 grid: the new rows
+    land in the caches bit for bit and the output matches the oracle."""
+    B, H, G, d, n_max = 128, 32, 8, 128, 520
+    announce(f"decode_append {B}x{H}/{G} d={d} N={n_max}")
+    x = synth.decode_append_inputs(B, H, G, d, n_max, seed=32, device=DEV, seqlens="uniform",
+                                   nan_tail=True)
+    scale = synth.scale_for(d)
+    k, v = x["k_cache"].clone(), x["v_cache"].clone()
+    out = gqa.decode_append(x["q"], x["k_new"], x["v_new"], k, v, x["seqlens"], scale=scale)
+    torch.cuda.synchronize()
+    ref, k_ref, v_ref = oracle.decode_append_ref(to64(x["q"]), to64(x["k_new"]), to64(x["v_new"]),
+                                                 to64(x["k_cache"]), to64(x["v_cache"]),
+                                                 x["seqlens"].cpu().numpy(), scale)
+    sl = x["seqlens"].cpu().numpy()
+    kk, vv = to64(k), to64(v)
+    for b in range(B):
+        pos = oracle.append_position(sl[b], n_max)
+        assert np.array_equal(kk[b, :, pos], k_ref[b, :, pos]), b
+        assert np.array_equal(vv[b, :, pos], v_ref[b, :, pos]), b
+    assert_close(out, ref, torch.bfloat16, "append, 1024-workgroup grid")
+
+
 def _slice64(t):
     """Exact float64 host copy of a (bf16 or f32) device slice (upcast on the GPU)."""
     return t.double().cpu().numpy()
