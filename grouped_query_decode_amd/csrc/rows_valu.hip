@@ -144,7 +144,9 @@ __global__ __launch_bounds__(256) void rows_valu_kernel(RowsProblem p) {
 
   // Positions in batches of kUnroll wave steps: all their loads are issued
   // before any of them is used, so the load latency is paid once per batch.
-  constexpr int kUnroll = 4;
+  // A one-head block has the registers for eight steps (the 128-position
+  // float32 decode then waits for one batch instead of two: 4.7 us, not 5.0).
+  constexpr int kUnroll = kHeadsPerBlock == 1 ? 8 : 4;
   for (int jb = j0 + wave * RPW; jb < j1; jb += kWaves * RPW * kUnroll) {
     float kf[kUnroll][EPL], vf[kUnroll][EPL];
     bool valid[kUnroll];
